@@ -1,0 +1,508 @@
+// C ABI of the DFlash draft-proposal path (declared in include/dflash.h): argument
+// validation, workspace planning and carve-up, and the launch sequence of each call.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/dflash.h"
+#include "kernels.h"
+
+using namespace dflash;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dflash_status fail(dflash_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+dflash_status fail(dflash_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dflash_status ok() {
+  g_last_error.clear();
+  return DFLASH_OK;
+}
+
+#define HIP_TRY(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess) return fail(DFLASH_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_bf16(const dflash_config *c) { return c->dtype == DFLASH_BF16; }
+size_t elem_size(const dflash_config *c) { return is_bf16(c) ? 2 : 4; }
+
+dflash_status check_config(const dflash_config *c) {
+  if (!c) return fail(DFLASH_ERR_INVALID_ARGUMENT, "config is NULL");
+  if (c->hidden <= 0 || c->n_layers < 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->intermediate <= 0 || c->vocab <= 0 || c->n_aux <= 0 || c->target_hidden <= 0 || c->block_size <= 0)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "config dimensions must be positive");
+  if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "unknown dtype %d", c->dtype);
+  if (c->n_q_heads % c->n_kv_heads != 0)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", c->n_q_heads,
+                c->n_kv_heads);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(DFLASH_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", c->head_dim);
+  if (c->hidden % 64 || c->intermediate % 64 || (c->n_aux * c->target_hidden) % 64 || c->target_hidden % 32)
+    return fail(DFLASH_ERR_UNSUPPORTED,
+                "hidden, intermediate and n_aux*target_hidden must be multiples of 64, target_hidden of 32");
+  if (c->vocab % 16) return fail(DFLASH_ERR_UNSUPPORTED, "vocab %d is not a multiple of 16", c->vocab);
+  if (c->block_size < 2 || c->block_size > 64)
+    return fail(DFLASH_ERR_UNSUPPORTED, "block_size %d outside [2, 64]", c->block_size);
+  if (c->block_size * (c->n_q_heads / c->n_kv_heads) > 64)
+    return fail(DFLASH_ERR_UNSUPPORTED, "block_size * q-heads per kv-head exceeds 64");
+  if (c->n_layers > 64) return fail(DFLASH_ERR_UNSUPPORTED, "more than 64 layers");
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "mask_token_id %d outside [0, vocab)", c->mask_token_id);
+  if (!(c->rms_eps >= 0.f)) return fail(DFLASH_ERR_INVALID_ARGUMENT, "rms_eps must be >= 0");
+  return DFLASH_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// Workspace plans. The same functions size the workspace and carve it at launch.
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+constexpr int kInjectChunk = 4096;  // rows per injection pass
+
+struct InjectPlan {
+  int rows, s_fc, s_kv;
+  size_t off_part, off_ctx, total;
+};
+
+InjectPlan plan_inject(const dflash_config *c, int rows) {
+  InjectPlan p{};
+  p.rows = rows;
+  const bool bf = is_bf16(c);
+  const int kvn = c->n_layers * 2 * c->n_kv_heads * c->head_dim;
+  p.s_fc = gemm_plan_splits(rows, c->hidden, c->n_aux * c->target_hidden, bf);
+  p.s_kv = gemm_plan_splits(rows, kvn, c->hidden, bf);
+  const size_t part = std::max((size_t)p.s_fc * rows * c->hidden, (size_t)p.s_kv * rows * kvn) * sizeof(float);
+  Carver cv;
+  p.off_part = cv.take(part);
+  p.off_ctx = cv.take((size_t)rows * c->hidden * elem_size(c));
+  p.total = cv.off;
+  return p;
+}
+
+struct ProposePlan {
+  int B, M, Mk;
+  int s_qkv, s_o, s_gu, s_down;
+  int chunk, nsplit, lm_groups;
+  size_t off_x, off_h, off_part, off_q, off_k, off_v, off_o, off_act, off_f, off_po, off_pm, off_pl, off_amv,
+      off_ami, total;
+};
+
+ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
+  ProposePlan p{};
+  const bool bf = is_bf16(c);
+  const int H = c->hidden, D = c->head_dim, QH = c->n_q_heads, KVH = c->n_kv_heads, I = c->intermediate;
+  const int K = c->block_size - 1;
+  p.B = B;
+  p.M = B * c->block_size;
+  p.Mk = B * K;
+  const int nqkv = (QH + 2 * KVH) * D;
+  p.s_qkv = gemm_plan_splits(p.M, nqkv, H, bf);
+  p.s_o = gemm_plan_splits(p.M, H, QH * D, bf);
+  p.s_gu = gemm_plan_splits(p.M, 2 * I, H, bf);
+  p.s_down = gemm_plan_splits(p.M, H, I, bf);
+  attn_plan(B, KVH, max_ctx + c->block_size, &p.chunk, &p.nsplit);
+  p.lm_groups = (c->vocab + 63) / 64;
+  const size_t es = elem_size(c);
+  const size_t part = std::max(std::max((size_t)p.s_qkv * nqkv, (size_t)p.s_o * H),
+                               std::max((size_t)p.s_gu * 2 * I, (size_t)p.s_down * H)) *
+                      p.M * sizeof(float);
+  Carver cv;
+  p.off_x = cv.take((size_t)p.M * H * sizeof(float));
+  p.off_h = cv.take((size_t)p.M * H * es);
+  p.off_part = cv.take(part);
+  p.off_q = cv.take((size_t)p.M * QH * D * es);
+  p.off_k = cv.take((size_t)p.M * KVH * D * es);
+  p.off_v = cv.take((size_t)p.M * KVH * D * es);
+  p.off_o = cv.take((size_t)p.M * QH * D * es);
+  p.off_act = cv.take((size_t)p.M * I * es);
+  p.off_f = cv.take((size_t)std::max(p.Mk, 1) * H * es);
+  const size_t nrow = (size_t)B * KVH * p.nsplit * 64;
+  p.off_po = cv.take(nrow * D * sizeof(float));
+  p.off_pm = cv.take(nrow * sizeof(float));
+  p.off_pl = cv.take(nrow * sizeof(float));
+  p.off_amv = cv.take((size_t)p.lm_groups * std::max(p.Mk, 1) * sizeof(float));
+  p.off_ami = cv.take((size_t)p.lm_groups * std::max(p.Mk, 1) * sizeof(int32_t));
+  p.total = cv.off;
+  return p;
+}
+
+template <typename P>
+P *at(void *ws, size_t off) {
+  return reinterpret_cast<P *>(static_cast<char *>(ws) + off);
+}
+
+dflash_status check_weights_common(const dflash_config *c, const dflash_weights *w) {
+  if (!w) return fail(DFLASH_ERR_INVALID_ARGUMENT, "weights is NULL");
+  if (!w->rope_cos || !w->rope_sin || w->rope_max_pos <= 0)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "RoPE table missing");
+  if (c->n_layers > 0 && !w->k_norm) return fail(DFLASH_ERR_INVALID_ARGUMENT, "k_norm array is NULL");
+  for (int l = 0; l < c->n_layers; ++l)
+    if (!w->k_norm[l]) return fail(DFLASH_ERR_INVALID_ARGUMENT, "k_norm[%d] is NULL", l);
+  return DFLASH_OK;
+}
+
+dflash_status check_cache(const dflash_config *c, const dflash_kv_cache *kv) {
+  if (!kv) return fail(DFLASH_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (kv->num_pages <= 0 || kv->page_size <= 0)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "cache num_pages and page_size must be positive");
+  if (c->n_layers > 0 && (!kv->k || !kv->v)) return fail(DFLASH_ERR_INVALID_ARGUMENT, "cache layer arrays are NULL");
+  for (int l = 0; l < c->n_layers; ++l)
+    if (!kv->k[l] || !kv->v[l]) return fail(DFLASH_ERR_INVALID_ARGUMENT, "cache of layer %d is NULL", l);
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+// =========================================================================================
+extern "C" {
+
+const char *dflash_status_string(int32_t st) {
+  switch (st) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DFLASH_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DFLASH_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DFLASH_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char *dflash_last_error(void) { return g_last_error.c_str(); }
+
+dflash_status dflash_build_rope_table(int32_t head_dim, double theta, int32_t max_pos, float *cos_out,
+                                      float *sin_out, void *stream) {
+  if (head_dim <= 0 || head_dim % 2) return fail(DFLASH_ERR_INVALID_ARGUMENT, "head_dim must be positive and even");
+  if (max_pos <= 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "max_pos must be positive");
+  if (!(theta > 0.0)) return fail(DFLASH_ERR_INVALID_ARGUMENT, "theta must be positive");
+  if (!cos_out || !sin_out) return fail(DFLASH_ERR_INVALID_ARGUMENT, "output is NULL");
+  HIP_TRY(launch_rope_table(head_dim, theta, max_pos, cos_out, sin_out, (hipStream_t)stream));
+  return ok();
+}
+
+dflash_status dflash_build_fused_kv_weight(const dflash_config *cfg, const dflash_weights *w, void *out,
+                                           void *stream) {
+  dflash_status st = check_config(cfg);
+  if (st != DFLASH_OK) return st;
+  if (!w || !out) return fail(DFLASH_ERR_INVALID_ARGUMENT, "weights or output is NULL");
+  if (cfg->n_layers > 0 && (!w->wk || !w->wv)) return fail(DFLASH_ERR_INVALID_ARGUMENT, "wk/wv arrays are NULL");
+  const size_t block = (size_t)cfg->n_kv_heads * cfg->head_dim * cfg->hidden * elem_size(cfg);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    if (!w->wk[l] || !w->wv[l]) return fail(DFLASH_ERR_INVALID_ARGUMENT, "wk/wv of layer %d is NULL", l);
+    char *dst = static_cast<char *>(out) + (size_t)(2 * l) * block;
+    HIP_TRY(hipMemcpyAsync(dst, w->wk[l], block, hipMemcpyDeviceToDevice, (hipStream_t)stream));
+    HIP_TRY(hipMemcpyAsync(dst + block, w->wv[l], block, hipMemcpyDeviceToDevice, (hipStream_t)stream));
+  }
+  return ok();
+}
+
+size_t dflash_workspace_bytes(const dflash_config *cfg, int32_t op, int32_t max_rows_or_batch,
+                              int32_t max_context) {
+  if (check_config(cfg) != DFLASH_OK || max_rows_or_batch < 0 || max_context < 0) return 0;
+  size_t best = kAlign;
+  if (op == DFLASH_OP_INJECT) {
+    const int cap = std::min<int>(max_rows_or_batch, kInjectChunk);
+    for (int r = 1; r <= cap; ++r) best = std::max(best, plan_inject(cfg, r).total);
+    return best;
+  }
+  if (op == DFLASH_OP_PROPOSE) {
+    for (int b = 1; b <= max_rows_or_batch; ++b) best = std::max(best, plan_propose(cfg, b, max_context).total);
+    return best;
+  }
+  return 0;
+}
+
+dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_weights *w,
+                                       const dflash_kv_cache *cache, const void *const *aux, int64_t aux_row_stride,
+                                       int32_t n_rows, const int32_t *positions, const int64_t *slot_mapping,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+  dflash_status st = check_config(cfg);
+  if (st != DFLASH_OK) return st;
+  if (n_rows < 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "n_rows < 0");
+  if (n_rows == 0) return ok();
+  if ((st = check_weights_common(cfg, w)) != DFLASH_OK) return st;
+  if ((st = check_cache(cfg, cache)) != DFLASH_OK) return st;
+  if (!w->fc || !w->hidden_norm || (cfg->n_layers > 0 && !w->kv_fused))
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "fc, hidden_norm or kv_fused is NULL");
+  if (!aux) return fail(DFLASH_ERR_INVALID_ARGUMENT, "aux is NULL");
+  for (int j = 0; j < cfg->n_aux; ++j)
+    if (!aux[j]) return fail(DFLASH_ERR_INVALID_ARGUMENT, "aux[%d] is NULL", j);
+  if (aux_row_stride < cfg->target_hidden)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "aux_row_stride %lld < target_hidden %d", (long long)aux_row_stride,
+                cfg->target_hidden);
+  const int vec = is_bf16(cfg) ? 8 : 4;
+  if (aux_row_stride % vec) return fail(DFLASH_ERR_UNSUPPORTED, "aux_row_stride must be a multiple of %d", vec);
+  if (!positions || !slot_mapping) return fail(DFLASH_ERR_INVALID_ARGUMENT, "positions or slot_mapping is NULL");
+  if (!workspace) return fail(DFLASH_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (cfg->n_aux > 8) return fail(DFLASH_ERR_UNSUPPORTED, "more than 8 auxiliary layers");
+  if (n_rows > 0 && cfg->n_layers == 0) return ok();  // nothing to write
+
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = is_bf16(cfg);
+  const size_t es = elem_size(cfg);
+  const int H = cfg->hidden, kvn = cfg->n_layers * 2 * cfg->n_kv_heads * cfg->head_dim;
+  for (int r0 = 0; r0 < n_rows; r0 += kInjectChunk) {
+    const int rows = std::min(kInjectChunk, n_rows - r0);
+    const InjectPlan p = plan_inject(cfg, rows);
+    if (p.total > workspace_bytes)
+      return fail(DFLASH_ERR_WORKSPACE_TOO_SMALL, "inject needs %zu workspace bytes, got %zu", p.total,
+                  workspace_bytes);
+    float *part = at<float>(workspace, p.off_part);
+    void *ctx = at<char>(workspace, p.off_ctx);
+
+    GemmArgs g{};
+    for (int j = 0; j < cfg->n_aux; ++j)
+      g.a[j] = static_cast<const char *>(aux[j]) + (size_t)r0 * aux_row_stride * es;
+    g.a_nseg = cfg->n_aux;
+    g.lda = aux_row_stride;
+    g.b[0] = w->fc;
+    g.b_end[0] = H;
+    g.b_nseg = 1;
+    g.M = rows;
+    g.N = H;
+    g.K = cfg->n_aux * cfg->target_hidden;
+    g.splits = p.s_fc;
+    g.part = part;
+    HIP_TRY(launch_gemm(g, bf, GemmEpi::kPartial, s));
+    HIP_TRY(launch_rmsnorm(bf, rows, H, nullptr, part, p.s_fc, w->hidden_norm, cfg->rms_eps, ctx, 0, nullptr, s));
+
+    GemmArgs k{};
+    k.a[0] = ctx;
+    k.a_nseg = 1;
+    k.lda = H;
+    k.b[0] = w->kv_fused;
+    k.b_end[0] = kvn;
+    k.b_nseg = 1;
+    k.M = rows;
+    k.N = kvn;
+    k.K = H;
+    k.splits = p.s_kv;
+    k.part = part;
+    HIP_TRY(launch_gemm(k, bf, GemmEpi::kPartial, s));
+
+    KvScatterArgs a{};
+    a.N = rows;
+    a.L = cfg->n_layers;
+    a.KVH = cfg->n_kv_heads;
+    a.D = cfg->head_dim;
+    a.part = part;
+    a.splits = p.s_kv;
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      a.k_norm[l] = w->k_norm[l];
+      a.k_cache[l] = cache->k[l];
+      a.v_cache[l] = cache->v[l];
+    }
+    a.eps = cfg->rms_eps;
+    a.rope_cos = w->rope_cos;
+    a.rope_sin = w->rope_sin;
+    a.rope_max_pos = w->rope_max_pos;
+    a.positions = positions + r0;
+    a.slot_mapping = slot_mapping + r0;
+    a.num_slots = (int64_t)cache->num_pages * cache->page_size;
+    HIP_TRY(launch_kv_scatter(bf, a, s));
+  }
+  return ok();
+}
+
+dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weights *w, const dflash_kv_cache *cache,
+                                   int32_t batch, const int32_t *bonus_tokens, const int32_t *seq_lens,
+                                   int32_t max_context, int32_t *draft_token_ids, int32_t *drafts_only,
+                                   void *hidden_out, void *workspace, size_t workspace_bytes, void *stream) {
+  dflash_status st = check_config(cfg);
+  if (st != DFLASH_OK) return st;
+  if (batch < 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "batch < 0");
+  if (batch == 0) return ok();
+  if (max_context < 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "max_context < 0");
+  if ((st = check_weights_common(cfg, w)) != DFLASH_OK) return st;
+  if ((st = check_cache(cfg, cache)) != DFLASH_OK) return st;
+  if (!cache->block_table || cache->max_blocks_per_seq <= 0)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "block_table is NULL or max_blocks_per_seq <= 0");
+  if (!w->embed || !w->lm_head || !w->final_norm) return fail(DFLASH_ERR_INVALID_ARGUMENT, "embed/lm_head/final_norm NULL");
+  const int L = cfg->n_layers;
+  if (L > 0 && (!w->in_norm || !w->wq || !w->wk || !w->wv || !w->q_norm || !w->wo || !w->post_norm || !w->w_gate ||
+                !w->w_up || !w->w_down))
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "a per-layer weight array is NULL");
+  for (int l = 0; l < L; ++l)
+    if (!w->in_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->q_norm[l] || !w->wo[l] || !w->post_norm[l] ||
+        !w->w_gate[l] || !w->w_up[l] || !w->w_down[l])
+      return fail(DFLASH_ERR_INVALID_ARGUMENT, "a weight of layer %d is NULL", l);
+  if (!bonus_tokens || !seq_lens || !draft_token_ids || !drafts_only || !workspace)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "an input/output pointer is NULL");
+
+  const ProposePlan p = plan_propose(cfg, batch, max_context);
+  if (p.total > workspace_bytes)
+    return fail(DFLASH_ERR_WORKSPACE_TOO_SMALL, "propose needs %zu workspace bytes, got %zu", p.total,
+                workspace_bytes);
+
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = is_bf16(cfg);
+  const int H = cfg->hidden, D = cfg->head_dim, QH = cfg->n_q_heads, KVH = cfg->n_kv_heads;
+  const int I = cfg->intermediate, bs = cfg->block_size, K = bs - 1, M = p.M;
+  float *x = at<float>(workspace, p.off_x);
+  void *h = at<char>(workspace, p.off_h);
+  float *part = at<float>(workspace, p.off_part);
+  void *q = at<char>(workspace, p.off_q);
+  void *kb = at<char>(workspace, p.off_k);
+  void *vb = at<char>(workspace, p.off_v);
+  void *o = at<char>(workspace, p.off_o);
+  void *act = at<char>(workspace, p.off_act);
+  void *f = at<char>(workspace, p.off_f);
+
+  HIP_TRY(launch_embed(bf, w->embed, cfg->vocab, H, bonus_tokens, batch, bs, cfg->mask_token_id, x, s));
+  int pending = 0;  // split count of the down-projection partials not yet added to x
+  for (int l = 0; l < L; ++l) {
+    HIP_TRY(launch_rmsnorm(bf, M, H, x, part, pending, w->in_norm[l], cfg->rms_eps, h, 0, nullptr, s));
+
+    GemmArgs g{};
+    g.a[0] = h;
+    g.a_nseg = 1;
+    g.lda = H;
+    g.b[0] = w->wq[l];
+    g.b[1] = w->wk[l];
+    g.b[2] = w->wv[l];
+    g.b_end[0] = QH * D;
+    g.b_end[1] = (QH + KVH) * D;
+    g.b_end[2] = (QH + 2 * KVH) * D;
+    g.b_nseg = 3;
+    g.M = M;
+    g.N = (QH + 2 * KVH) * D;
+    g.K = H;
+    g.splits = p.s_qkv;
+    g.part = part;
+    HIP_TRY(launch_gemm(g, bf, GemmEpi::kPartial, s));
+    HIP_TRY(launch_qk_norm_rope(bf, M, bs, QH, KVH, D, part, p.s_qkv, w->q_norm[l], w->k_norm[l], cfg->rms_eps,
+                                w->rope_cos, w->rope_sin, w->rope_max_pos, seq_lens, max_context, q, kb, vb, s));
+
+    AttnArgs at_{};
+    at_.q = q;
+    at_.kb = kb;
+    at_.vb = vb;
+    at_.kc = cache->k[l];
+    at_.vc = cache->v[l];
+    at_.block_table = cache->block_table;
+    at_.maxb = cache->max_blocks_per_seq;
+    at_.P = cache->page_size;
+    at_.num_pages = cache->num_pages;
+    at_.seq_lens = seq_lens;
+    at_.max_ctx = max_context;
+    at_.B = batch;
+    at_.bs = bs;
+    at_.QH = QH;
+    at_.KVH = KVH;
+    at_.D = D;
+    at_.chunk = p.chunk;
+    at_.nsplit = p.nsplit;
+    at_.po = at<float>(workspace, p.off_po);
+    at_.pm = at<float>(workspace, p.off_pm);
+    at_.pl = at<float>(workspace, p.off_pl);
+    at_.o = o;
+    HIP_TRY(launch_attention(bf, at_, s));
+
+    GemmArgs go{};
+    go.a[0] = o;
+    go.a_nseg = 1;
+    go.lda = QH * D;
+    go.b[0] = w->wo[l];
+    go.b_end[0] = H;
+    go.b_nseg = 1;
+    go.M = M;
+    go.N = H;
+    go.K = QH * D;
+    go.splits = p.s_o;
+    go.part = part;
+    HIP_TRY(launch_gemm(go, bf, GemmEpi::kPartial, s));
+    HIP_TRY(launch_rmsnorm(bf, M, H, x, part, p.s_o, w->post_norm[l], cfg->rms_eps, h, 0, nullptr, s));
+
+    GemmArgs gu{};
+    gu.a[0] = h;
+    gu.a_nseg = 1;
+    gu.lda = H;
+    gu.b[0] = w->w_gate[l];
+    gu.b[1] = w->w_up[l];
+    gu.b_end[0] = I;
+    gu.b_end[1] = 2 * I;
+    gu.b_nseg = 2;
+    gu.M = M;
+    gu.N = 2 * I;
+    gu.K = H;
+    gu.splits = p.s_gu;
+    gu.part = part;
+    HIP_TRY(launch_gemm(gu, bf, GemmEpi::kPartial, s));
+    HIP_TRY(launch_swiglu(bf, M, I, part, p.s_gu, act, s));
+
+    GemmArgs gd{};
+    gd.a[0] = act;
+    gd.a_nseg = 1;
+    gd.lda = I;
+    gd.b[0] = w->w_down[l];
+    gd.b_end[0] = H;
+    gd.b_nseg = 1;
+    gd.M = M;
+    gd.N = H;
+    gd.K = I;
+    gd.splits = p.s_down;
+    gd.part = part;
+    HIP_TRY(launch_gemm(gd, bf, GemmEpi::kPartial, s));
+    pending = p.s_down;
+  }
+  // final norm on the drafted rows (block slots 1..K), compacted to [B*K, H]
+  HIP_TRY(launch_rmsnorm(bf, M, H, x, part, pending, w->final_norm, cfg->rms_eps, f, bs, hidden_out, s));
+
+  GemmArgs gl{};
+  gl.a[0] = f;
+  gl.a_nseg = 1;
+  gl.lda = H;
+  gl.b[0] = w->lm_head;
+  gl.b_end[0] = cfg->vocab;
+  gl.b_nseg = 1;
+  gl.M = p.Mk;
+  gl.N = cfg->vocab;
+  gl.K = H;
+  gl.splits = 1;
+  gl.amax_val = at<float>(workspace, p.off_amv);
+  gl.amax_idx = at<int32_t>(workspace, p.off_ami);
+  HIP_TRY(launch_gemm(gl, bf, GemmEpi::kArgmax, s));
+  HIP_TRY(launch_argmax_reduce(batch, K, p.lm_groups, gl.amax_val, gl.amax_idx, bonus_tokens, cfg->vocab,
+                               draft_token_ids, drafts_only, s));
+  return ok();
+}
+
+dflash_status dflash_greedy_verify(int32_t batch, int32_t num_drafts, const int32_t *draft_tokens,
+                                   const int32_t *target_tokens, int32_t *accepted_len, int32_t *output_tokens,
+                                   int32_t *next_bonus, void *stream) {
+  if (batch < 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "batch < 0");
+  if (num_drafts < 1 || num_drafts > 63) return fail(DFLASH_ERR_UNSUPPORTED, "num_drafts %d outside [1, 63]", num_drafts);
+  if (batch == 0) return ok();
+  if (!draft_tokens || !target_tokens || !accepted_len || !output_tokens || !next_bonus)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "an input/output pointer is NULL");
+  HIP_TRY(launch_verify(batch, num_drafts, draft_tokens, target_tokens, accepted_len, output_tokens, next_bonus,
+                        (hipStream_t)stream));
+  return ok();
+}
+
+}  // extern "C"

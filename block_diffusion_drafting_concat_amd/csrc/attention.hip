@@ -1,0 +1,253 @@
+// Non-causal paged block attention of the DFlash drafter.
+//
+// Every query of a sequence's block sees the sequence's c_b context keys (from the paged
+// cache) plus all bs block keys, with no mask. Work-group = (sequence b, kv head g, split s):
+// its bs*G query rows (the G q-heads sharing kv head g, times the bs block positions) share
+// every K/V tile it loads, so each KV byte is read from HBM once per work-group. The key
+// range c_b + bs is cut into splits of `chunk` keys so that one long context (32k) still
+// spreads over the whole chip; split partials (unnormalised output, running max, running
+// sum) are merged by a second kernel with the usual log-sum-exp rescaling.
+//
+// MFMA layout. Scores are computed transposed, S^T = K Q^T (A = K tile rows, B = Q rows), so
+// each lane ends up holding 4 keys of one query row. The output is computed as O^T = V^T P^T,
+// where P^T is the B operand. The key order inside each MFMA is permuted so that the 4+4
+// keys a lane holds after two score tiles are exactly the 8 consecutive keys the P^T operand
+// needs: P never leaves registers. V is staged transposed in LDS so V^T fragments are
+// 16-byte LDS reads. P is fed to the bf16 MFMA as a hi/lo pair (p = hi + lo, both bf16),
+// which keeps the probabilities at ~16 bits of precision.
+#include <float.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dflash {
+namespace {
+
+constexpr int kTileKeys = 64;
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
+  constexpr int KPV = Storage<T>::kPerVec;
+  constexpr int CH = 4 * KPV;                // contraction elements per MFMA step
+  constexpr int NB = KPV / 4;                // score tiles per P.V step
+  constexpr int KSTR = D + KPV;              // K row stride in LDS (16-byte pad)
+  constexpr int VSTR = kTileKeys + KPV;      // V^T row stride in LDS
+  constexpr int CPR = D / KPV;               // 16-byte vectors per key row
+  __shared__ __attribute__((aligned(16))) T ks[kTileKeys * KSTR];
+  __shared__ __attribute__((aligned(16))) T vts[D * VSTR];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = a.QH / a.KVH;
+  const int R = a.bs * G;
+  const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
+  const int T_total = c + a.bs;
+  const int kbeg = split * a.chunk;
+  if (kbeg >= T_total) return;  // nothing for this split
+  const int kend = min(T_total, kbeg + a.chunk);
+
+  // Query fragment (B operand of S^T): row r = hh*bs + j of this wave's 16-row tile.
+  const int r = wave * 16 + (lane & 15);
+  const bool rvalid = r < R && wave * 16 < R;
+  Vec16 qf[D / CH];
+  {
+    const int hh = r / a.bs, j = r % a.bs;
+    const T *qp = reinterpret_cast<const T *>(a.q) +
+                  ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + (lane >> 4) * KPV;
+#pragma unroll
+    for (int dc = 0; dc < D / CH; ++dc) qf[dc] = rvalid ? load_vec16(qp + dc * CH) : zero_vec16();
+  }
+
+  f32x4_t acc_o[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) acc_o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float scale = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
+
+  const T *kc = reinterpret_cast<const T *>(a.kc);
+  const T *vc = reinterpret_cast<const T *>(a.vc);
+  const T *kbk = reinterpret_cast<const T *>(a.kb);
+  const T *vbk = reinterpret_cast<const T *>(a.vb);
+  const int32_t *bt = a.block_table + (size_t)b * a.maxb;
+
+  for (int t0 = kbeg; t0 < kend; t0 += kTileKeys) {
+    // ---- stage the K tile (row-major) and V tile (transposed) in LDS
+    __syncthreads();
+    for (int v = threadIdx.x; v < kTileKeys * CPR; v += 256) {
+      const int key = v / CPR, part = v % CPR;
+      const int t = t0 + key;
+      Vec16 kv = zero_vec16(), vv = zero_vec16();
+      if (t < kend) {
+        const T *ksrc, *vsrc;
+        if (t < c) {
+          int page = bt[min(t / a.P, a.maxb - 1)];
+          page = min(max(page, 0), a.num_pages - 1);
+          const size_t off = ((size_t)(page * a.P + t % a.P) * a.KVH + g) * D + part * KPV;
+          ksrc = kc + off;
+          vsrc = vc + off;
+        } else {
+          const size_t off = ((size_t)(b * a.bs + (t - c)) * a.KVH + g) * D + part * KPV;
+          ksrc = kbk + off;
+          vsrc = vbk + off;
+        }
+        kv = load_vec16(ksrc);
+        vv = load_vec16(vsrc);
+      }
+      *reinterpret_cast<uint4 *>(&ks[key * KSTR + part * KPV]) = kv.u;
+      T ve[KPV];
+      __builtin_memcpy(ve, &vv.u, 16);
+#pragma unroll
+      for (int e = 0; e < KPV; ++e) vts[(part * KPV + e) * VSTR + key] = ve[e];
+    }
+    __syncthreads();
+    if (wave * 16 >= R) continue;
+
+    // ---- S^T tiles: 4 tiles of 16 keys; tile sb row rho holds key
+    //      (sb / NB) * CH + KPV * (rho / 4) + 4 * (sb % NB) + rho % 4
+    f32x4_t s[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      s[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int rho = lane & 15;
+      const int key = (sb / NB) * CH + KPV * (rho / 4) + 4 * (sb % NB) + rho % 4;
+#pragma unroll
+      for (int dc = 0; dc < D / CH; ++dc) {
+        const Vec16 kf = load_vec16(&ks[key * KSTR + dc * CH + (lane >> 4) * KPV]);
+        mma16<T>(s[sb], kf, qf[dc]);
+      }
+    }
+    // lane (group gq = lane/16) holds, for its row, keys (sb/NB)*CH + KPV*gq + 4*(sb%NB) + i
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = (sb / NB) * CH + KPV * (lane >> 4) + 4 * (sb % NB) + i;
+        const float v = (t0 + key < kend) ? s[sb][i] * scale : -INFINITY;
+        s[sb][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) acc_o[i] *= alpha;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = (s[sb][i] == -INFINITY) ? 0.f : exp2f(s[sb][i] - m_new);
+        s[sb][i] = p;
+        l_run += p;
+      }
+
+    // ---- O^T += V^T P^T, one P.V step per CH keys
+#pragma unroll
+    for (int ps = 0; ps < 4 / NB; ++ps) {
+      if constexpr (KPV == 8) {
+        uint16_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = s[ps * 2 + e / 4][e % 4];
+          hi[e] = f32_to_bf16(p);
+          lo[e] = f32_to_bf16(p - bf16_to_f32(hi[e]));
+        }
+        Vec16 phi, plo;
+        __builtin_memcpy(&phi.u, hi, 16);
+        __builtin_memcpy(&plo.u, lo, 16);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          const Vec16 vf = load_vec16(&vts[(db * 16 + (lane & 15)) * VSTR + ps * CH + (lane >> 4) * KPV]);
+          mma16<T>(acc_o[db], vf, phi);
+          mma16<T>(acc_o[db], vf, plo);
+        }
+      } else {
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = s[ps][e];
+        Vec16 pf;
+        __builtin_memcpy(&pf.u, pv, 16);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          const Vec16 vf = load_vec16(&vts[(db * 16 + (lane & 15)) * VSTR + ps * CH + (lane >> 4) * KPV]);
+          mma16<T>(acc_o[db], vf, pf);
+        }
+      }
+    }
+  }
+  if (wave * 16 >= R) return;
+
+  // ---- partials: O^T lane layout is d = db*16 + (lane/16)*4 + i, row = lane%16
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  const size_t base = ((size_t)(b * a.KVH + g) * a.nsplit + split) * 64;
+  if (rvalid) {
+    float *po = a.po + (base + r) * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) po[db * 16 + (lane >> 4) * 4 + i] = acc_o[db][i];
+    if (lane < 16) {
+      a.pm[base + r] = m_run;
+      a.pl[base + r] = l_run;
+    }
+  }
+}
+
+// Merge the split partials of one (sequence, kv head, query row); one thread per element.
+template <typename T>
+__global__ void attn_merge_kernel(AttnArgs a) {
+  const int row = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = a.QH / a.KVH;
+  const int D = a.D;
+  const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
+  const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
+  const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64;
+  float mmax = -INFINITY;
+  for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, a.pm[base + s * 64 + row]);
+  const int hh = row / a.bs, j = row % a.bs;
+  T *o = reinterpret_cast<T *>(a.o) + ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float w = exp2f(a.pm[base + s * 64 + row] - mmax);
+      num += w * a.po[(base + s * 64 + row) * D + d];
+      den += w * a.pl[base + s * 64 + row];
+    }
+    Storage<T>::store(o, d, num / den);
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
+  dim3 grid(a.nsplit, a.KVH, a.B);
+  if (a.D == 128)
+    attn_partial_kernel<T, 128><<<grid, 256, 0, s>>>(a);
+  else
+    attn_partial_kernel<T, 64><<<grid, 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int G = a.QH / a.KVH;
+  attn_merge_kernel<T><<<dim3(a.bs * G, a.KVH, a.B), a.D, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void attn_plan(int B, int KVH, int max_keys, int *chunk, int *nsplit) {
+  // Aim for ~1024 work-groups in total, in splits of at least one 64-key tile.
+  long want = (long)max_keys * B * KVH / 1024;
+  int ch = (int)((want + kTileKeys - 1) / kTileKeys) * kTileKeys;
+  if (ch < kTileKeys) ch = kTileKeys;
+  *chunk = ch;
+  *nsplit = (max_keys + ch - 1) / ch;
+}
+
+hipError_t launch_attention(bool bf16, const AttnArgs &a, hipStream_t s) {
+  return bf16 ? launch_t<uint16_t>(a, s) : launch_t<float>(a, s);
+}
+
+}  // namespace dflash

@@ -1,0 +1,296 @@
+// Row-wise kernels of the DFlash path: block embedding, RMSNorm (with the split-K partial
+// sum and residual add folded in), q/k RMSNorm + RoPE of the block, the context K/V
+// epilogue of injection (k_norm + RoPE + paged scatter), SwiGLU, the LM-head argmax
+// reduction, greedy verification and the RoPE table.
+#include <float.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dflash {
+namespace {
+
+// ---------------------------------------------------------------------------------------
+// Block construction + embedding: row m = b*bs + j gets embed[bonus[b]] for j == 0 and
+// embed[mask] otherwise, converted to the fp32 residual stream.
+template <typename T>
+__global__ void embed_kernel(const T *embed, int V, int H, const int32_t *bonus, int bs, int mask_id,
+                             float *x) {
+  const int m = blockIdx.x;
+  const int b = m / bs, j = m % bs;
+  int id = (j == 0) ? bonus[b] : mask_id;
+  id = min(max(id, 0), V - 1);
+  const T *src = embed + (size_t)id * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) x[(size_t)m * H + i] = Storage<T>::load(src, i);
+}
+
+// ---------------------------------------------------------------------------------------
+// r = resid[m] + sum_s part[s][m]; resid[m] = r; out = round(r / rms(r) * w).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int M, int H, float *resid, const float *part,
+                                                      int splits, const T *w, float eps, T *out,
+                                                      int keep_bs, T *hidden_out) {
+  __shared__ float red[16];
+  extern __shared__ float row[];
+  const int m = blockIdx.x;
+  if (keep_bs > 0 && m % keep_bs == 0) return;  // block slot 0 is not drafted
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    float v = resid ? resid[(size_t)m * H + i] : 0.f;
+    for (int s = 0; s < splits; ++s) v += part[((size_t)s * M + m) * H + i];
+    row[i] = v;
+    ss += v * v;
+  }
+  ss = block_sum(ss, red);
+  const float inv = rsqrtf(ss / (float)H + eps);
+  const int orow = keep_bs > 0 ? (m / keep_bs) * (keep_bs - 1) + m % keep_bs - 1 : m;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    const float v = row[i];
+    if (resid && splits > 0) resid[(size_t)m * H + i] = v;
+    const float y = v * inv * Storage<T>::load(w, i);
+    Storage<T>::store(out, (size_t)orow * H + i, y);
+    if (hidden_out) Storage<T>::store(hidden_out, (size_t)orow * H + i, y);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Per-head RMSNorm + rotate-half RoPE of one head vector held by one wave (D <= 128, so each
+// lane owns the pair (i, i + D/2) for i = lane < D/2).
+__device__ __forceinline__ void norm_rope_pair(float &x1, float &x2, bool own, int D, float w1, float w2,
+                                               float eps, float cs, float sn) {
+  const float ss = wave_sum(own ? x1 * x1 + x2 * x2 : 0.f);
+  const float inv = rsqrtf(ss / (float)D + eps);
+  const float a = x1 * inv * w1, b = x2 * inv * w2;
+  x1 = a * cs - b * sn;
+  x2 = b * cs + a * sn;
+}
+
+// One wave per (row, head). Heads [0, QH) are q, [QH, QH+KVH) k, then v.
+template <typename T>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(int M, int bs, int QH, int KVH, int D,
+                                                           const float *part, int splits, const T *q_norm,
+                                                           const T *k_norm, float eps, const float *rope_cos,
+                                                           const float *rope_sin, int rope_max_pos,
+                                                           const int32_t *seq_lens, int max_ctx, T *q, T *k,
+                                                           T *v) {
+  const int lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nh = QH + 2 * KVH;
+  if (wid >= M * nh) return;
+  const int m = wid / nh, h = wid % nh;
+  const int N = nh * D, half = D / 2;
+  const bool own = lane < half;
+  const int i1 = own ? lane : 0, i2 = i1 + half;
+  float x1 = 0.f, x2 = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float *p = part + ((size_t)s * M + m) * N + (size_t)h * D;
+    x1 += p[i1];
+    x2 += p[i2];
+  }
+  if (h >= QH + KVH) {  // value head: round only
+    if (own) {
+      T *dst = v + ((size_t)m * KVH + (h - QH - KVH)) * D;
+      Storage<T>::store(dst, i1, x1);
+      Storage<T>::store(dst, i2, x2);
+    }
+    return;
+  }
+  const T *w = h < QH ? q_norm : k_norm;
+  const int b = m / bs, j = m % bs;
+  const int c = min(max(seq_lens[b], 0), max_ctx);
+  const int pos = min(c + j, rope_max_pos - 1);
+  const float cs = rope_cos[(size_t)pos * half + i1], sn = rope_sin[(size_t)pos * half + i1];
+  norm_rope_pair(x1, x2, own, D, Storage<T>::load(w, i1), Storage<T>::load(w, i2), eps, cs, sn);
+  if (own) {
+    T *dst = h < QH ? q + ((size_t)m * QH + h) * D : k + ((size_t)m * KVH + (h - QH)) * D;
+    Storage<T>::store(dst, i1, x1);
+    Storage<T>::store(dst, i2, x2);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Context K/V epilogue of injection: one wave per (row, layer, head-of-2*KVH).
+template <typename T>
+__global__ __launch_bounds__(256) void kv_scatter_kernel(KvScatterArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int per_row = a.L * 2 * a.KVH;
+  if (wid >= a.N * per_row) return;
+  const int r = wid / per_row, rem = wid % per_row;
+  const int l = rem / (2 * a.KVH), kvh = rem % (2 * a.KVH);
+  const bool is_v = kvh >= a.KVH;
+  const int g = is_v ? kvh - a.KVH : kvh;
+  const int64_t slot = a.slot_mapping[r];
+  if (slot < 0 || slot >= a.num_slots) return;  // padding row / out of range: skipped
+  const int D = a.D, half = D / 2;
+  const int ncol = per_row * D;
+  const bool own = lane < half;
+  const int i1 = own ? lane : 0, i2 = i1 + half;
+  const size_t col = (size_t)(l * 2 * a.KVH + kvh) * D;
+  float x1 = 0.f, x2 = 0.f;
+  for (int s = 0; s < a.splits; ++s) {
+    const float *p = a.part + ((size_t)s * a.N + r) * ncol + col;
+    x1 += p[i1];
+    x2 += p[i2];
+  }
+  if (!is_v) {
+    const T *w = reinterpret_cast<const T *>(a.k_norm[l]);
+    const int pos = min(max(a.positions[r], 0), a.rope_max_pos - 1);
+    const float cs = a.rope_cos[(size_t)pos * half + i1], sn = a.rope_sin[(size_t)pos * half + i1];
+    norm_rope_pair(x1, x2, own, D, Storage<T>::load(w, i1), Storage<T>::load(w, i2), a.eps, cs, sn);
+  }
+  if (own) {
+    T *dst = reinterpret_cast<T *>(is_v ? a.v_cache[l] : a.k_cache[l]) + ((size_t)slot * a.KVH + g) * D;
+    Storage<T>::store(dst, i1, x1);
+    Storage<T>::store(dst, i2, x2);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <typename T>
+__global__ void swiglu_kernel(int M, int I, const float *part, int splits, T *act) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)M * I) return;
+  const int m = idx / I, n = idx % I;
+  float gsum = 0.f, usum = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float *p = part + ((size_t)s * M + m) * (2 * (size_t)I);
+    gsum += p[n];
+    usum += p[I + n];
+  }
+  const float silu = gsum / (1.f + expf(-gsum));
+  Storage<T>::store(act, idx, silu * usum);
+}
+
+// ---------------------------------------------------------------------------------------
+// One thread per drafted row: reduce the per-64-column (max, index) pairs, lowest index on
+// ties, then assemble [bonus, drafts].
+__global__ void argmax_reduce_kernel(int B, int K, int ngroups, const float *val, const int32_t *idx,
+                                     const int32_t *bonus, int V, int32_t *draft_ids, int32_t *drafts_only) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  const int Mr = B * K;
+  if (r >= Mr) return;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int gi = 0; gi < ngroups; ++gi) argmax_merge(best, bi, val[(size_t)gi * Mr + r], idx[(size_t)gi * Mr + r]);
+  if (bi == 0x7fffffff) bi = 0;  // every logit NaN: unspecified, but a valid id
+  const int b = r / K, j = r % K;
+  drafts_only[(size_t)b * K + j] = bi;
+  draft_ids[(size_t)b * (K + 1) + j + 1] = bi;
+  if (j == 0) draft_ids[(size_t)b * (K + 1)] = min(max(bonus[b], 0), V - 1);
+}
+
+// ---------------------------------------------------------------------------------------
+// Greedy verification: one wave per sequence; lane i compares draft i with target i and the
+// first mismatch (lowest set bit of the ballot) ends the accepted prefix.
+__global__ void verify_kernel(int B, int K, const int32_t *drafts, const int32_t *target, int32_t *acc,
+                              int32_t *out, int32_t *next_bonus) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (b >= B) return;
+  const bool mismatch = lane < K && drafts[(size_t)b * K + lane] != target[(size_t)b * (K + 1) + lane];
+  const unsigned long long mask = __ballot(mismatch);
+  const int n = mask ? (int)__builtin_ctzll(mask) : K;  // accepted drafts
+  const int a = n + 1;
+  if (lane <= K) out[(size_t)b * (K + 1) + lane] = lane < a ? target[(size_t)b * (K + 1) + lane] : -1;
+  if (lane == 0) {
+    acc[b] = a;
+    next_bonus[b] = target[(size_t)b * (K + 1) + n];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+__global__ void rope_table_kernel(int D, double theta, int max_pos, float *cs, float *sn) {
+  const int half = D / 2;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)max_pos * half) return;
+  const int p = idx / half, i = idx % half;
+  const double inv_freq = pow(theta, -2.0 * (double)i / (double)D);
+  const double ang = (double)p * inv_freq;
+  cs[idx] = (float)cos(ang);
+  sn[idx] = (float)sin(ang);
+}
+
+}  // namespace
+
+// ===========================================================================================
+hipError_t launch_embed(bool bf16, const void *embed, int V, int H, const int32_t *bonus, int B, int bs,
+                        int mask_id, float *x, hipStream_t s) {
+  if (bf16)
+    embed_kernel<uint16_t><<<B * bs, 256, 0, s>>>((const uint16_t *)embed, V, H, bonus, bs, mask_id, x);
+  else
+    embed_kernel<float><<<B * bs, 256, 0, s>>>((const float *)embed, V, H, bonus, bs, mask_id, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(bool bf16, int M, int H, float *resid, const float *part, int splits, const void *w,
+                          float eps, void *out, int keep_bs, void *hidden_out, hipStream_t s) {
+  const size_t lds = (size_t)H * sizeof(float);
+  if (bf16)
+    rmsnorm_kernel<uint16_t><<<M, 256, lds, s>>>(M, H, resid, part, splits, (const uint16_t *)w, eps,
+                                                  (uint16_t *)out, keep_bs, (uint16_t *)hidden_out);
+  else
+    rmsnorm_kernel<float><<<M, 256, lds, s>>>(M, H, resid, part, splits, (const float *)w, eps, (float *)out,
+                                              keep_bs, (float *)hidden_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_norm_rope(bool bf16, int M, int bs, int QH, int KVH, int D, const float *part, int splits,
+                               const void *q_norm, const void *k_norm, float eps, const float *rope_cos,
+                               const float *rope_sin, int rope_max_pos, const int32_t *seq_lens, int max_ctx,
+                               void *q, void *k, void *v, hipStream_t s) {
+  const int waves = M * (QH + 2 * KVH);
+  const int grid = (waves + 3) / 4;
+  if (bf16)
+    qk_norm_rope_kernel<uint16_t><<<grid, 256, 0, s>>>(M, bs, QH, KVH, D, part, splits, (const uint16_t *)q_norm,
+                                                       (const uint16_t *)k_norm, eps, rope_cos, rope_sin,
+                                                       rope_max_pos, seq_lens, max_ctx, (uint16_t *)q,
+                                                       (uint16_t *)k, (uint16_t *)v);
+  else
+    qk_norm_rope_kernel<float><<<grid, 256, 0, s>>>(M, bs, QH, KVH, D, part, splits, (const float *)q_norm,
+                                                    (const float *)k_norm, eps, rope_cos, rope_sin, rope_max_pos,
+                                                    seq_lens, max_ctx, (float *)q, (float *)k, (float *)v);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_scatter(bool bf16, const KvScatterArgs &a, hipStream_t s) {
+  const long waves = (long)a.N * a.L * 2 * a.KVH;
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  if (bf16)
+    kv_scatter_kernel<uint16_t><<<grid, 256, 0, s>>>(a);
+  else
+    kv_scatter_kernel<float><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(bool bf16, int M, int I, const float *part, int splits, void *act, hipStream_t s) {
+  const size_t n = (size_t)M * I;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (bf16)
+    swiglu_kernel<uint16_t><<<grid, 256, 0, s>>>(M, I, part, splits, (uint16_t *)act);
+  else
+    swiglu_kernel<float><<<grid, 256, 0, s>>>(M, I, part, splits, (float *)act);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_reduce(int B, int K, int ngroups, const float *val, const int32_t *idx,
+                                const int32_t *bonus, int V, int32_t *draft_ids, int32_t *drafts_only,
+                                hipStream_t s) {
+  const int n = B * K;
+  argmax_reduce_kernel<<<(n + 63) / 64, 64, 0, s>>>(B, K, ngroups, val, idx, bonus, V, draft_ids, drafts_only);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(int B, int K, const int32_t *drafts, const int32_t *target, int32_t *acc, int32_t *out,
+                         int32_t *next_bonus, hipStream_t s) {
+  verify_kernel<<<(B + 3) / 4, 256, 0, s>>>(B, K, drafts, target, acc, out, next_bonus);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(int D, double theta, int max_pos, float *cos_out, float *sin_out, hipStream_t s) {
+  const size_t n = (size_t)max_pos * (D / 2);
+  rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(D, theta, max_pos, cos_out, sin_out);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,112 @@
+"""Shared set-up of the GPU parity tests: a drafter on the device, its paged cache filled by
+the HIP injection, and the oracle's own cache for the sequences a test checks."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from block_diffusion_drafting_concat_amd import binding, synth
+from oracle import dflash_oracle as O
+
+
+def lazy_numpy(W):
+    """Mapping name -> exact fp32 numpy array, converted on first use."""
+    class _M(dict):
+        def __missing__(self, k):
+            v = synth.as_f32(W[k])
+            self[k] = v
+            return v
+    return _M()
+
+
+def rel_err(got, want):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    return float(np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-30))
+
+
+def check_close(spec, got, want, what=""):
+    """fp32 drafters: max-abs 1e-4; bf16 drafters: per-tensor max-abs relative 2e-2."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if spec.dtype == "f32":
+        err = float(np.max(np.abs(got - want))) if got.size else 0.0
+        assert err <= 1e-4, f"{what}: max abs err {err}"
+    else:
+        err = rel_err(got, want) if got.size else 0.0
+        assert err <= 2e-2, f"{what}: relative err {err}"
+    return err
+
+
+def mode_of(spec):
+    return "bf16" if spec.dtype == "bf16" else "f32"
+
+
+class Setup:
+    """Device drafter + cache with every sequence's context injected by the HIP path."""
+
+    def __init__(self, spec, ctx, page_size=16, shuffle=False, seed=0, extra_pages=2, canary=None,
+                 inject_chunk=None):
+        self.spec, self.seed = spec, seed
+        self.ctx = np.asarray(ctx, np.int32)
+        self.B = len(ctx)
+        self.W = synth.make_weights(spec, seed)
+        maxb = (int(self.ctx.max()) + spec.block_size + page_size - 1) // page_size
+        ids = np.arange(self.B * maxb)
+        if shuffle:
+            ids = np.random.default_rng(seed + 17).permutation(self.B * maxb + extra_pages)[: self.B * maxb]
+        self.bt = ids.reshape(self.B, maxb).astype(np.int32)
+        self.num_pages = self.B * maxb + extra_pages
+        self.P = page_size
+        self.max_ctx = int(self.ctx.max())
+        self.dev = binding.Drafter(spec, self.W, rope_max_pos=self.max_ctx + spec.block_size + 1)
+        self.cache = binding.PagedCache(spec, self.num_pages, page_size,
+                                        torch.from_numpy(self.bt).cuda())
+        if canary is not None:
+            for t in self.cache.k + self.cache.v:
+                t.fill_(canary)
+        chunk = inject_chunk or 4096
+        self.ws_inject = self.dev.workspace(binding.DFLASH_OP_INJECT, min(chunk, max(1, int(self.ctx.max()))))
+        for b in range(self.B):
+            c = int(self.ctx[b])
+            for r0 in range(0, c, chunk):
+                n = min(chunk, c - r0)
+                self.inject_rows(b, r0, n)
+        self.ws_prop = self.dev.workspace(binding.DFLASH_OP_PROPOSE, self.B, self.max_ctx)
+        torch.cuda.synchronize()
+
+    def slots(self, b, pos):
+        return O.paged_slots(self.bt, np.full(len(pos), b), np.asarray(pos), self.P)
+
+    def inject_rows(self, b, r0, n):
+        aux = [a.cuda() for a in synth.aux_states_fast(self.spec, self.seed, b, r0, n)]
+        pos = np.arange(r0, r0 + n, dtype=np.int32)
+        slots = self.slots(b, pos).astype(np.int64)
+        self.dev.inject(self.cache, aux, torch.from_numpy(pos).cuda(), torch.from_numpy(slots).cuda(), self.ws_inject)
+
+    def propose(self, bonus, hidden=True):
+        spec = self.spec
+        bonus_d = torch.from_numpy(np.asarray(bonus, np.int32)).cuda()
+        ctx_d = torch.from_numpy(self.ctx).cuda()
+        hid = torch.empty((self.B * (spec.block_size - 1), spec.hidden), dtype=binding.storage_dtype(spec),
+                          device="cuda") if hidden else None
+        ids, drafts = self.dev.propose(self.cache, bonus_d, ctx_d, self.max_ctx, self.ws_prop, hidden_out=hid)
+        torch.cuda.synchronize()
+        return ids.cpu().numpy(), drafts.cpu().numpy(), (None if hid is None else hid.float().cpu().numpy())
+
+    # -- oracle side
+    def oracle_cache(self, seqs, Wn):
+        """Oracle caches holding the context of the sequences `seqs` (others stay empty)."""
+        spec = self.spec
+        shape = (self.num_pages, self.P, spec.n_kv_heads, spec.head_dim)
+        kc = [np.zeros(shape, np.float32) for _ in range(spec.n_layers)]
+        vc = [np.zeros(shape, np.float32) for _ in range(spec.n_layers)]
+        for b in seqs:
+            c = int(self.ctx[b])
+            for r0 in range(0, c, 4096):
+                n = min(4096, c - r0)
+                aux = [synth.as_f32(a) for a in synth.aux_states_fast(spec, self.seed, b, r0, n)]
+                pos = np.arange(r0, r0 + n)
+                O.inject_context_kv(spec, Wn, kc, vc, aux, pos, self.slots(b, pos), mode_of(spec))
+        return kc, vc

@@ -1,0 +1,94 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_drafting_concat_amd import binding, synth
+from oracle import dflash_oracle as O
+from tests.gpu_helpers import Setup, check_close, lazy_numpy, mode_of
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = synth.DrafterSpec(hidden=256, n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                               intermediate=512, vocab=2048, n_aux=2, target_hidden=192, block_size=16,
+                               mask_token_id=2047, rope_theta=1e6, dtype="bf16")
+TINY = synth.WORKLOADS["tiny_fp32_b1"].spec
+
+
+def _compare_drafts(spec, got_ids, got_drafts, ref, bonus, what):
+    gap = ref["gap"]
+    clear = gap >= 1e-2
+    assert np.array_equal(got_ids[:, 0], np.asarray(bonus)), what
+    assert np.array_equal(got_drafts[clear], ref["drafts_only"][clear]), (
+        what, np.argwhere((got_drafts != ref["drafts_only"]) & clear))
+    assert np.array_equal(got_ids[:, 1:], got_drafts)
+    return int((~clear).sum())
+
+
+def _compare_cache(spec, st, kc, vc, seqs):
+    for b in seqs:
+        pos = np.arange(int(st.ctx[b]))
+        sl = st.slots(b, pos)
+        for l in range(spec.n_layers):
+            gk = st.cache.k[l].float().cpu().numpy().reshape(-1, spec.n_kv_heads, spec.head_dim)[sl]
+            gv = st.cache.v[l].float().cpu().numpy().reshape(-1, spec.n_kv_heads, spec.head_dim)[sl]
+            ok = kc[l].reshape(-1, spec.n_kv_heads, spec.head_dim)[sl]
+            ov = vc[l].reshape(-1, spec.n_kv_heads, spec.head_dim)[sl]
+            check_close(spec, gk, ok, f"K layer {l} seq {b}")
+            check_close(spec, gv, ov, f"V layer {l} seq {b}")
+
+
+@pytest.mark.parametrize("spec,ctx,P,shuffle", [
+    (TINY, [128], 16, False),
+    (TINY, [0, 37, 200], 16, True),
+    (SMALL_BF16, [300], 16, False),
+    (SMALL_BF16, [0, 5, 64, 257], 16, True),
+    (SMALL_BF16, [77, 130], 1, True),
+])
+def test_inject_and_propose_match_oracle(spec, ctx, P, shuffle):
+    print(f"\n[case] spec={spec.dtype} H={spec.hidden} ctx={ctx} P={P}", flush=True)
+    st = Setup(spec, ctx, page_size=P, shuffle=shuffle, seed=1, canary=3.0)
+    Wn = lazy_numpy(st.W)
+    kc, vc = st.oracle_cache(range(st.B), Wn)
+    _compare_cache(spec, st, kc, vc, range(st.B))
+    # pages outside every sequence's context keep the canary
+    used = np.zeros(st.num_pages * P, bool)
+    for b in range(st.B):
+        used[st.slots(b, np.arange(int(st.ctx[b])))] = True
+    for t in st.cache.k + st.cache.v:
+        flat = t.float().cpu().numpy().reshape(st.num_pages * P, -1)
+        assert np.all(flat[~used] == 3.0)
+
+    bonus = (np.arange(st.B) * 31 + 7) % spec.vocab
+    ids, drafts, hid = st.propose(bonus)
+    ref = O.propose_block(spec, Wn, kc, vc, st.bt, bonus, st.ctx, mode_of(spec), page_size=P)
+    _compare_drafts(spec, ids, drafts, ref, bonus, "propose")
+    check_close(spec, hid, ref["hidden"], "final hidden")
+
+
+def test_propose_is_deterministic_and_batch_invariant():
+    spec = SMALL_BF16
+    st = Setup(spec, [40, 300, 0, 129], page_size=16, shuffle=True, seed=2)
+    bonus = np.array([5, 1000, 2047, 0])
+    a = st.propose(bonus)
+    b = st.propose(bonus)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)  # bit-identical reruns
+
+
+def test_verify_matches_oracle_bit_exact():
+    rng = np.random.default_rng(0)
+    for B, K, V in [(1, 7, 4096), (32, 15, 151936), (128, 9, 128256), (5, 1, 3), (64, 63, 5)]:
+        d = rng.integers(0, V, size=(B, K)).astype(np.int32)
+        t = rng.integers(0, V, size=(B, K + 1)).astype(np.int32)
+        # force assorted accepted lengths, including all-match and none
+        for b in range(B):
+            n = rng.integers(0, K + 1)
+            t[b, :n] = d[b, :n]
+        t[0, :K] = d[0]
+        acc, out, nb = binding.verify(torch.from_numpy(d).cuda(), torch.from_numpy(t).cuda())
+        torch.cuda.synchronize()
+        ra, ro, rn = O.greedy_verify(d, t)
+        assert np.array_equal(acc.cpu().numpy(), ra)
+        assert np.array_equal(out.cpu().numpy(), ro)
+        assert np.array_equal(nb.cpu().numpy(), rn)
