@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Throughput of the DFlash draft-proposal path on one MI355X.
+
+One step is the whole path on one batch: inject the step's new context rows into every draft
+layer's KV cache, propose one block per sequence, and greedily verify the drafts against
+synthetic target tokens. The default workload is the Qwen3-8B-shaped bf16 drafter at batch 1,
+block size 16 (15 drafts), a 2048-token context and 16 injected rows per step. Weights and
+inputs are seeded synthetic data, resident in HBM before timing starts.
+
+Prints one JSON line (stdout): drafted tokens/s as `value`, draft blocks/s, the
+weight-streaming GEMM kernel's roofline, and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from block_diffusion_drafting_concat_amd import binding, synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+# Profile tags of the launches of gemm_kernel<bf16, MT=1, partial, one A segment>, the
+# weight-streaming GEMM that dominates a batch-1 step.
+STREAM_GEMM_TAGS = ("gemm.qkv", "gemm.o", "gemm.gate_up", "gemm.down", "gemm.kv")
+GEMM_SOURCES = ("block_diffusion_drafting_concat_amd/csrc/gemm.hip", "block_diffusion_drafting_concat_amd/csrc/common.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------------------------
+# Algorithmic bytes: what the method must move, independent of how the kernels tile it.
+# ---------------------------------------------------------------------------------------------
+def gemm_roles(spec, M_prop: int, M_inj: int):
+    """{tag: (M, N, K)} of every projection of one step (per launch)."""
+    H, D, QH, KVH, I, L = (spec.hidden, spec.head_dim, spec.n_q_heads, spec.n_kv_heads, spec.intermediate,
+                           spec.n_layers)
+    return {
+        "gemm.fc": (M_inj, H, spec.n_aux * spec.target_hidden),
+        "gemm.kv": (M_inj, L * 2 * KVH * D, H),
+        "gemm.qkv": (M_prop, (QH + 2 * KVH) * D, H),
+        "gemm.o": (M_prop, H, QH * D),
+        "gemm.gate_up": (M_prop, 2 * I, H),
+        "gemm.down": (M_prop, H, I),
+    }
+
+
+def gemm_bytes(M, N, K, es):
+    """Weights read once + activations read once + fp32 result written once."""
+    return N * K * es + M * K * es + M * N * 4
+
+
+def step_bytes(spec, B, ctx, n_inject):
+    """Algorithmic HBM bytes of one whole step (inject + propose + verify)."""
+    es = 2 if spec.dtype == "bf16" else 4
+    H, D, KVH, L, V = spec.hidden, spec.head_dim, spec.n_kv_heads, spec.n_layers, spec.vocab
+    bs, K = spec.block_size, spec.block_size - 1
+    M, N = B * bs, B * n_inject
+    roles = gemm_roles(spec, M, N)
+    tot = gemm_bytes(*roles["gemm.fc"], es) + gemm_bytes(*roles["gemm.kv"], es)
+    tot += N * L * 2 * KVH * D * es  # cache writes
+    tot += L * sum(gemm_bytes(*roles[t], es) for t in ("gemm.qkv", "gemm.o", "gemm.gate_up", "gemm.down"))
+    tot += L * int(np.sum(ctx)) * 2 * KVH * D * es  # context K/V read by attention
+    tot += M * H * es + V * H * es + B * K * H * es  # embedding rows, LM head, its input
+    tot += B * (2 * K + 1) * 4 * 2  # token ids in/out
+    return tot
+
+
+def source_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per launch of the streaming GEMM from the committed rocprofv3 --pmc summary,
+    or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"gemm_stream_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_sha") != source_sha(GEMM_SOURCES):
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------------------------
+class Bench:
+    def __init__(self, wl: synth.Workload):
+        self.wl, self.spec = wl, wl.spec
+        spec = self.spec
+        t0 = time.time()
+        self.W = synth.make_weights(spec, wl.seed)
+        log(f"[bench] weights drawn in {time.time() - t0:.1f}s")
+        self.ctx = synth.context_lengths(wl)
+        self.B = wl.batch
+        self.layout = synth.page_layout(wl, self.ctx)
+        self.max_ctx = int(self.ctx.max())
+        self.dev = binding.Drafter(spec, self.W, rope_max_pos=self.max_ctx + spec.block_size + 1)
+        self.cache = binding.PagedCache(spec, self.layout.num_pages, self.layout.page_size,
+                                        torch.from_numpy(self.layout.block_table).cuda())
+        n = wl.inject_rows
+        self.ws_inj = self.dev.workspace(binding.DFLASH_OP_INJECT, max(self.B * n, 4096))
+        self.ws_prop = self.dev.workspace(binding.DFLASH_OP_PROPOSE, self.B, self.max_ctx)
+        t0 = time.time()
+        for b in range(self.B):  # prefill every context
+            c = int(self.ctx[b])
+            for r0 in range(0, c, 4096):
+                self._inject_host(b, r0, min(4096, c - r0))
+        torch.cuda.synchronize()
+        log(f"[bench] prefill injected {int(self.ctx.sum())} rows in {time.time() - t0:.1f}s")
+        # per-step inputs: the last n context rows of every sequence (re-injected each step)
+        rows = [(b, int(self.ctx[b]) - n) for b in range(self.B)]
+        aux = [synth.aux_states(spec, wl.seed, b, r0, n) for b, r0 in rows]
+        self.step_aux = [torch.cat([a[j] for a in aux]).cuda() for j in range(spec.n_aux)]
+        pos = np.concatenate([np.arange(r0, r0 + n) for _, r0 in rows]).astype(np.int32)
+        bt, P = self.layout.block_table, self.layout.page_size
+        slots = np.concatenate([bt[b, np.minimum(np.arange(r0, r0 + n) // P, bt.shape[1] - 1)] * P
+                                + np.arange(r0, r0 + n) % P for b, r0 in rows]).astype(np.int64)
+        self.step_pos = torch.from_numpy(pos).cuda()
+        self.step_slots = torch.from_numpy(slots).cuda()
+        self.bonus = torch.from_numpy(synth.bonus_tokens(wl)).cuda()
+        self.seq_lens = torch.from_numpy(self.ctx).cuda()
+        K = spec.block_size - 1
+        self.out = (torch.empty((self.B, K + 1), dtype=torch.int32, device="cuda"),
+                    torch.empty((self.B, K), dtype=torch.int32, device="cuda"))
+        self.vout = (torch.empty(self.B, dtype=torch.int32, device="cuda"),
+                     torch.empty((self.B, K + 1), dtype=torch.int32, device="cuda"),
+                     torch.empty(self.B, dtype=torch.int32, device="cuda"))
+        # synthetic target tokens from the drafts of a first step
+        self.target = torch.zeros((self.B, K + 1), dtype=torch.int32, device="cuda")
+        self.step()
+        torch.cuda.synchronize()
+        self.target = torch.from_numpy(synth.target_tokens(wl, self.out[1].cpu().numpy())).cuda()
+
+    def _inject_host(self, b, r0, n):
+        aux = [a.cuda() for a in synth.aux_states_fast(self.spec, self.wl.seed, b, r0, n)]
+        pos = np.arange(r0, r0 + n, dtype=np.int32)
+        bt, P = self.layout.block_table, self.layout.page_size
+        slots = (bt[b, np.minimum(pos // P, bt.shape[1] - 1)] * P + pos % P).astype(np.int64)
+        self.dev.inject(self.cache, aux, torch.from_numpy(pos).cuda(), torch.from_numpy(slots).cuda(), self.ws_inj)
+
+    def step(self):
+        self.dev.inject(self.cache, self.step_aux, self.step_pos, self.step_slots, self.ws_inj)
+        self.dev.propose(self.cache, self.bonus, self.seq_lens, self.max_ctx, self.ws_prop, out=self.out)
+        binding.verify(self.out[1], self.target, out=self.vout)
+
+    def timed(self, steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+
+# ---------------------------------------------------------------------------------------------
+def cpu_baseline(bench: Bench):
+    """The CPU oracle timed on this host on one step of the same workload (one sequence: the
+    first), after an untimed oracle prefill of that sequence's context."""
+    from oracle import dflash_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    spec, wl = bench.spec, bench.wl
+    mode = "bf16" if spec.dtype == "bf16" else "f32"
+
+    class _Lazy(dict):
+        def __missing__(self, k):
+            v = synth.as_f32(bench.W[k])
+            self[k] = v
+            return v
+
+    Wn = _Lazy()
+    b, c, n = 0, int(bench.ctx[0]), wl.inject_rows
+    lay = bench.layout
+    shape = (lay.num_pages, lay.page_size, spec.n_kv_heads, spec.head_dim)
+    kc = [np.zeros(shape, np.float32) for _ in range(spec.n_layers)]
+    vc = [np.zeros(shape, np.float32) for _ in range(spec.n_layers)]
+    bt = lay.block_table[b:b + 1]
+    t0 = time.time()
+    for r0 in range(0, c - n, 1024):
+        m = min(1024, c - n - r0)
+        aux = [synth.as_f32(a) for a in synth.aux_states_fast(spec, wl.seed, b, r0, m)]
+        pos = np.arange(r0, r0 + m)
+        O.inject_context_kv(spec, Wn, kc, vc, aux, pos, O.paged_slots(bt, np.zeros(m, int), pos, lay.page_size),
+                            mode)
+    log(f"[bench] oracle prefill {c - n} rows in {time.time() - t0:.1f}s")
+    aux = [synth.as_f32(a) for a in synth.aux_states(spec, wl.seed, b, c - n, n)]
+    pos = np.arange(c - n, c)
+    slots = O.paged_slots(bt, np.zeros(n, int), pos, lay.page_size)
+    bonus = bench.bonus.cpu().numpy()[:1]
+    t0 = time.perf_counter()
+    O.inject_context_kv(spec, Wn, kc, vc, aux, pos, slots, mode)
+    res = O.propose_block(spec, Wn, kc, vc, bt, bonus, bench.ctx[:1], mode)
+    O.greedy_verify(res["drafts_only"], bench.target.cpu().numpy()[:1])
+    dt = time.perf_counter() - t0
+    K = spec.block_size - 1
+    return {"value": K / dt, "unit": "drafted tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 step (inject {n} rows + propose + verify) of sequence 0 of {wl.name}, fp64 numpy",
+            "seconds_per_step": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3_8b_b1_ctx2048", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run one 1 GiB device copy (scale reference for rocprofv3 byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the drafting path of this build is "
+              "single-GPU; see the sharding design for multi-GPU.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    spec = wl.spec
+    bench = Bench(wl)
+    for _ in range(args.warmup):
+        bench.step()
+    torch.cuda.synchronize()
+
+    # timed region; every library launch is bracketed by hipEvents on its stream
+    binding.profile_reset()
+    binding.profile_enable(True)
+    sec = bench.timed(args.steps)
+    binding.profile_enable(False)
+    prof = binding.profile_collect()
+    sec_plain = bench.timed(args.steps)  # same steps without events, for the event overhead
+
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    B, K = bench.B, spec.block_size - 1
+    es = 2 if spec.dtype == "bf16" else 4
+    roles = gemm_roles(spec, B * spec.block_size, B * wl.inject_rows)
+    launches_per_step = {t: (spec.n_layers if t in ("gemm.qkv", "gemm.o", "gemm.gate_up", "gemm.down") else 1)
+                         for t in roles}
+    g_bytes = sum(gemm_bytes(*roles[t], es) * launches_per_step[t] for t in STREAM_GEMM_TAGS) * args.steps
+    g_launch = sum(prof.get(t, (0, 0.0))[0] for t in STREAM_GEMM_TAGS)
+    g_ms = sum(prof.get(t, (0, 0.0))[1] for t in STREAM_GEMM_TAGS)
+    achieved = g_bytes / (g_ms * 1e-3) / 1e9 if g_ms > 0 else 0.0
+    traffic = load_traffic(wl.name)
+    sbytes = step_bytes(spec, B, bench.ctx, wl.inject_rows)
+    result = {
+        "metric": "drafted tokens/sec and draft blocks/sec (Qwen3-8B-shape, b16); % HBM/MFMA roofline",
+        "value": B * K / sec,
+        "unit": "drafted tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded random-weight drafter, N(0,1) aux states)",
+        "config": {"workload": wl.name, "batch": B, "block_size": spec.block_size, "drafts_per_block": K,
+                   "context": [int(wl.ctx_lo), int(wl.ctx_hi)], "inject_rows_per_seq": wl.inject_rows,
+                   "hidden": spec.hidden, "layers": spec.n_layers, "heads": [spec.n_q_heads, spec.n_kv_heads],
+                   "head_dim": spec.head_dim, "intermediate": spec.intermediate, "vocab": spec.vocab,
+                   "fc_in": spec.n_aux * spec.target_hidden, "page_size": wl.page_size},
+        "draft_blocks_per_s": B / sec,
+        "ms_per_step_without_events": sec_plain * 1e3,
+        "step_roofline": {"bound": "hbm", "algorithmic_bytes": sbytes, "achieved": sbytes / sec / 1e9,
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": sbytes / sec / 1e9 / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "kernel": "gemm_kernel<bf16,MT=1,partial,one A segment> (weight streaming)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "launches": g_launch,
+                     "avg_launch_us": (g_ms / g_launch * 1e3) if g_launch else None,
+                     "algorithmic_bytes_per_launch": g_bytes / g_launch if g_launch else None},
+        "kernel_ms_per_step": {k: v[1] / args.steps for k, v in sorted(prof.items())},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(bench)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

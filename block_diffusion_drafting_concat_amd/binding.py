@@ -74,6 +74,13 @@ def lib() -> ctypes.CDLL:
         for fn in ("dflash_build_rope_table", "dflash_build_fused_kv_weight", "dflash_inject_context_kv",
                    "dflash_propose_block", "dflash_greedy_verify"):
             getattr(L, fn).restype = _i32
+        L.dflash_profile_enable.argtypes = [_i32]
+        L.dflash_profile_enable.restype = _i32
+        L.dflash_profile_collect.restype = _i32
+        L.dflash_profile_count.restype = _i32
+        L.dflash_profile_entry.argtypes = [_i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
+                                           ctypes.POINTER(ctypes.c_double)]
+        L.dflash_profile_entry.restype = _i32
         L.dflash_status_string.argtypes = [_i32]
         L.dflash_status_string.restype = ctypes.c_char_p
         L.dflash_last_error.restype = ctypes.c_char_p
@@ -220,6 +227,26 @@ class Drafter:
         propose_block(self.cfg, self.struct, cache.struct, B, bonus, seq_lens, max_context, out[0], out[1],
                       hidden_out, workspace, stream)
         return out
+
+
+def profile_enable(on: bool) -> None:
+    _check(lib().dflash_profile_enable(1 if on else 0))
+
+
+def profile_reset() -> None:
+    lib().dflash_profile_reset()
+
+
+def profile_collect() -> dict:
+    """Wait for the recorded launch events; returns {kernel name: (launches, total ms)}."""
+    L = lib()
+    _check(L.dflash_profile_collect())
+    out = {}
+    for i in range(L.dflash_profile_count()):
+        name, n, ms = ctypes.c_char_p(), ctypes.c_int64(), ctypes.c_double()
+        _check(L.dflash_profile_entry(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)))
+        out[name.value.decode()] = (int(n.value), float(ms.value))
+    return out
 
 
 def verify(drafts, target, out=None, stream=None):

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdflash.so")
-SOURCES = ["api.cpp", "gemm.hip", "attention.hip", "rowwise.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "gemm.hip", "attention.hip", "rowwise.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are kept out of every kernel (hipcc would otherwise form them
 # from plain float code).

@@ -288,6 +288,7 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
     g.K = cfg->n_aux * cfg->target_hidden;
     g.splits = p.s_fc;
     g.part = part;
+    g.tag = "gemm.fc";
     HIP_TRY(launch_gemm(g, bf, GemmEpi::kPartial, s));
     HIP_TRY(launch_rmsnorm(bf, rows, H, nullptr, part, p.s_fc, w->hidden_norm, cfg->rms_eps, ctx, 0, nullptr, s));
 
@@ -303,6 +304,7 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
     k.K = H;
     k.splits = p.s_kv;
     k.part = part;
+    k.tag = "gemm.kv";
     HIP_TRY(launch_gemm(k, bf, GemmEpi::kPartial, s));
 
     KvScatterArgs a{};
@@ -394,6 +396,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     g.K = H;
     g.splits = p.s_qkv;
     g.part = part;
+    g.tag = "gemm.qkv";
     HIP_TRY(launch_gemm(g, bf, GemmEpi::kPartial, s));
     HIP_TRY(launch_qk_norm_rope(bf, M, bs, QH, KVH, D, part, p.s_qkv, w->q_norm[l], w->k_norm[l], cfg->rms_eps,
                                 w->rope_cos, w->rope_sin, w->rope_max_pos, seq_lens, max_context, q, kb, vb, s));
@@ -435,6 +438,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     go.K = QH * D;
     go.splits = p.s_o;
     go.part = part;
+    go.tag = "gemm.o";
     HIP_TRY(launch_gemm(go, bf, GemmEpi::kPartial, s));
     HIP_TRY(launch_rmsnorm(bf, M, H, x, part, p.s_o, w->post_norm[l], cfg->rms_eps, h, 0, nullptr, s));
 
@@ -452,6 +456,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     gu.K = H;
     gu.splits = p.s_gu;
     gu.part = part;
+    gu.tag = "gemm.gate_up";
     HIP_TRY(launch_gemm(gu, bf, GemmEpi::kPartial, s));
     HIP_TRY(launch_swiglu(bf, M, I, part, p.s_gu, act, s));
 
@@ -467,6 +472,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     gd.K = I;
     gd.splits = p.s_down;
     gd.part = part;
+    gd.tag = "gemm.down";
     HIP_TRY(launch_gemm(gd, bf, GemmEpi::kPartial, s));
     pending = p.s_down;
   }
@@ -484,6 +490,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
   gl.N = cfg->vocab;
   gl.K = H;
   gl.splits = 1;
+  gl.tag = "gemm.lm_head";
   gl.amax_val = at<float>(workspace, p.off_amv);
   gl.amax_idx = at<int32_t>(workspace, p.off_ami);
   HIP_TRY(launch_gemm(gl, bf, GemmEpi::kArgmax, s));

@@ -224,14 +224,20 @@ __global__ void attn_merge_kernel(AttnArgs a) {
 template <typename T>
 hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
   dim3 grid(a.nsplit, a.KVH, a.B);
-  if (a.D == 128)
-    attn_partial_kernel<T, 128><<<grid, 256, 0, s>>>(a);
-  else
-    attn_partial_kernel<T, 64><<<grid, 256, 0, s>>>(a);
+  {
+    ProfScope prof("attn_partial", s);
+    if (a.D == 128)
+      attn_partial_kernel<T, 128><<<grid, 256, 0, s>>>(a);
+    else
+      attn_partial_kernel<T, 64><<<grid, 256, 0, s>>>(a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = a.QH / a.KVH;
-  attn_merge_kernel<T><<<dim3(a.bs * G, a.KVH, a.B), a.D, 0, s>>>(a);
+  {
+    ProfScope prof("attn_merge", s);
+    attn_merge_kernel<T><<<dim3(a.bs * G, a.KVH, a.B), a.D, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

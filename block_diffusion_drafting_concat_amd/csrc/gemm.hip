@@ -167,6 +167,7 @@ int gemm_plan_splits(int M, int N, int K, bool bf16) {
 }
 
 hipError_t launch_gemm(const GemmArgs &g, bool bf16, GemmEpi epi, hipStream_t s) {
+  ProfScope prof(g.tag ? g.tag : "gemm", s);
   return bf16 ? launch_dt<uint16_t>(g, epi, s) : launch_dt<float>(g, epi, s);
 }
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "profile.h"
+
 namespace dflash {
 
 // ------------------------------------------------------------------------------------------
@@ -28,6 +30,7 @@ struct GemmArgs {
   float *part;        // [splits][M][N]
   float *amax_val;    // [ceil(N/64)][M]
   int32_t *amax_idx;  // [ceil(N/64)][M]
+  const char *tag;    // name under which the launch is timed when profiling is on
 };
 
 enum class GemmEpi { kPartial, kArgmax };

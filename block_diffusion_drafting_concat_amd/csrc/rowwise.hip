@@ -216,6 +216,7 @@ __global__ void rope_table_kernel(int D, double theta, int max_pos, float *cs, f
 // ===========================================================================================
 hipError_t launch_embed(bool bf16, const void *embed, int V, int H, const int32_t *bonus, int B, int bs,
                         int mask_id, float *x, hipStream_t s) {
+  ProfScope prof("embed", s);
   if (bf16)
     embed_kernel<uint16_t><<<B * bs, 256, 0, s>>>((const uint16_t *)embed, V, H, bonus, bs, mask_id, x);
   else
@@ -225,6 +226,7 @@ hipError_t launch_embed(bool bf16, const void *embed, int V, int H, const int32_
 
 hipError_t launch_rmsnorm(bool bf16, int M, int H, float *resid, const float *part, int splits, const void *w,
                           float eps, void *out, int keep_bs, void *hidden_out, hipStream_t s) {
+  ProfScope prof("rmsnorm", s);
   const size_t lds = (size_t)H * sizeof(float);
   if (bf16)
     rmsnorm_kernel<uint16_t><<<M, 256, lds, s>>>(M, H, resid, part, splits, (const uint16_t *)w, eps,
@@ -239,6 +241,7 @@ hipError_t launch_qk_norm_rope(bool bf16, int M, int bs, int QH, int KVH, int D,
                                const void *q_norm, const void *k_norm, float eps, const float *rope_cos,
                                const float *rope_sin, int rope_max_pos, const int32_t *seq_lens, int max_ctx,
                                void *q, void *k, void *v, hipStream_t s) {
+  ProfScope prof("qk_norm_rope", s);
   const int waves = M * (QH + 2 * KVH);
   const int grid = (waves + 3) / 4;
   if (bf16)
@@ -254,6 +257,7 @@ hipError_t launch_qk_norm_rope(bool bf16, int M, int bs, int QH, int KVH, int D,
 }
 
 hipError_t launch_kv_scatter(bool bf16, const KvScatterArgs &a, hipStream_t s) {
+  ProfScope prof("kv_scatter", s);
   const long waves = (long)a.N * a.L * 2 * a.KVH;
   const unsigned grid = (unsigned)((waves + 3) / 4);
   if (bf16)
@@ -264,6 +268,7 @@ hipError_t launch_kv_scatter(bool bf16, const KvScatterArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_swiglu(bool bf16, int M, int I, const float *part, int splits, void *act, hipStream_t s) {
+  ProfScope prof("swiglu", s);
   const size_t n = (size_t)M * I;
   const unsigned grid = (unsigned)((n + 255) / 256);
   if (bf16)
@@ -276,6 +281,7 @@ hipError_t launch_swiglu(bool bf16, int M, int I, const float *part, int splits,
 hipError_t launch_argmax_reduce(int B, int K, int ngroups, const float *val, const int32_t *idx,
                                 const int32_t *bonus, int V, int32_t *draft_ids, int32_t *drafts_only,
                                 hipStream_t s) {
+  ProfScope prof("argmax_reduce", s);
   const int n = B * K;
   argmax_reduce_kernel<<<(n + 63) / 64, 64, 0, s>>>(B, K, ngroups, val, idx, bonus, V, draft_ids, drafts_only);
   return hipGetLastError();
@@ -283,11 +289,13 @@ hipError_t launch_argmax_reduce(int B, int K, int ngroups, const float *val, con
 
 hipError_t launch_verify(int B, int K, const int32_t *drafts, const int32_t *target, int32_t *acc, int32_t *out,
                          int32_t *next_bonus, hipStream_t s) {
+  ProfScope prof("verify", s);
   verify_kernel<<<(B + 3) / 4, 256, 0, s>>>(B, K, drafts, target, acc, out, next_bonus);
   return hipGetLastError();
 }
 
 hipError_t launch_rope_table(int D, double theta, int max_pos, float *cos_out, float *sin_out, hipStream_t s) {
+  ProfScope prof("rope_table", s);
   const size_t n = (size_t)max_pos * (D / 2);
   rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(D, theta, max_pos, cos_out, sin_out);
   return hipGetLastError();

@@ -53,7 +53,7 @@ typedef enum dflash_op { DFLASH_OP_INJECT = 0, DFLASH_OP_PROPOSE = 1 } dflash_op
  * concatenated auxiliary states, target embedding and LM head; the DFlashConfig fields
  * block size and mask token id). Supported: head_dim 64 or 128; hidden, intermediate and
  * n_aux*target_hidden multiples of 64; n_q_heads a multiple of n_kv_heads; 2 <= block_size
- * and block_size*n_q_heads/n_kv_heads <= 128; block_size - 1 <= 63 drafts. */
+ * and block_size*n_q_heads/n_kv_heads <= 64 (so block_size - 1 <= 63 drafts). */
 typedef struct dflash_config {
   int32_t hidden;         /* H */
   int32_t n_layers;       /* L */
@@ -181,6 +181,19 @@ dflash_status dflash_greedy_verify(int32_t batch, int32_t num_drafts,
                                    const int32_t *draft_tokens, const int32_t *target_tokens,
                                    int32_t *accepted_len, int32_t *output_tokens,
                                    int32_t *next_bonus, void *stream);
+
+/* Per-kernel timing, for measurement tools. While enabled, every kernel the library launches
+ * is bracketed by two hipEvents recorded on the launch's stream. dflash_profile_collect
+ * waits for the recorded events and adds each launch's duration to the totals of its kernel
+ * (by kernel name). Disabled by default, when no event is recorded. Process-wide and
+ * thread-safe. Enabling creates events (host-side runtime objects); the drafting calls still
+ * allocate no device memory. */
+dflash_status dflash_profile_enable(int32_t on);
+dflash_status dflash_profile_collect(void);
+void dflash_profile_reset(void);
+int32_t dflash_profile_count(void); /* number of distinct kernel names with totals */
+/* Totals of entry i < dflash_profile_count(): name (static string), launches, milliseconds. */
+dflash_status dflash_profile_entry(int32_t i, const char **name, int64_t *launches, double *total_ms);
 
 const char *dflash_status_string(int32_t status);
 const char *dflash_last_error(void); /* thread-local; "" when the last call succeeded */
