@@ -28,9 +28,14 @@ import torch  # noqa: E402
 from block_diffusion_drafting_concat_amd import binding, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-# Profile tags of the launches of gemm_kernel<bf16, MT=1, partial, one A segment>, the
-# weight-streaming GEMM that dominates a batch-1 step.
-STREAM_GEMM_TAGS = ("gemm.qkv", "gemm.o", "gemm.gate_up", "gemm.down", "gemm.kv")
+# GEMM kernel instances (by epilogue) and the profiling tags of their launches in a step.
+GEMM_KERNELS = {
+    "gemm_kernel<bf16,MT=1,CW=4,KW=2,kStore>": ("gemm.qkv", "gemm.kv"),
+    "gemm_kernel<bf16,MT=1,CW=4,KW=2,kResidAdd>": ("gemm.o", "gemm.down"),
+    "gemm_kernel<bf16,MT=1,CW=4,KW=2,kSwiGLU>": ("gemm.gate_up",),
+    "gemm_kernel<bf16,MT=1,CW=8,KW=1,kArgmax>": ("gemm.lm_head",),
+    "gemm_kernel<bf16,MT=1,CW=4,KW=2,kStore,multi-A>": ("gemm.fc",),
+}
 GEMM_SOURCES = ("block_diffusion_drafting_concat_amd/csrc/gemm.hip", "block_diffusion_drafting_concat_amd/csrc/common.h")
 
 
@@ -47,6 +52,7 @@ def gemm_roles(spec, M_prop: int, M_inj: int):
                            spec.n_layers)
     return {
         "gemm.fc": (M_inj, H, spec.n_aux * spec.target_hidden),
+        "gemm.lm_head": (M_prop // spec.block_size * (spec.block_size - 1), spec.vocab, H),
         "gemm.kv": (M_inj, L * 2 * KVH * D, H),
         "gemm.qkv": (M_prop, (QH + 2 * KVH) * D, H),
         "gemm.o": (M_prop, H, QH * D),
@@ -60,6 +66,17 @@ def gemm_bytes(M, N, K, es):
     return N * K * es + M * K * es + M * N * 4
 
 
+def tag_bytes(spec, tag, M, N, K, es):
+    """Algorithmic bytes of one launch of a tagged projection (see DESIGN: roofline)."""
+    if tag == "gemm.gate_up":  # N = 2I: gate and up weights, the normalised rows, the product
+        return N * K * es + M * K * es + M * (N // 2) * es
+    if tag in ("gemm.o", "gemm.down"):  # residual stream read and written
+        return N * K * es + M * K * es + 2 * M * N * 4
+    if tag == "gemm.lm_head":  # logits are never stored
+        return N * K * es + M * K * es
+    return gemm_bytes(M, N, K, es)
+
+
 def step_bytes(spec, B, ctx, n_inject):
     """Algorithmic HBM bytes of one whole step (inject + propose + verify)."""
     es = 2 if spec.dtype == "bf16" else 4
@@ -67,11 +84,11 @@ def step_bytes(spec, B, ctx, n_inject):
     bs, K = spec.block_size, spec.block_size - 1
     M, N = B * bs, B * n_inject
     roles = gemm_roles(spec, M, N)
-    tot = gemm_bytes(*roles["gemm.fc"], es) + gemm_bytes(*roles["gemm.kv"], es)
+    tot = tag_bytes(spec, "gemm.fc", *roles["gemm.fc"], es) + tag_bytes(spec, "gemm.kv", *roles["gemm.kv"], es)
     tot += N * L * 2 * KVH * D * es  # cache writes
-    tot += L * sum(gemm_bytes(*roles[t], es) for t in ("gemm.qkv", "gemm.o", "gemm.gate_up", "gemm.down"))
+    tot += L * sum(tag_bytes(spec, t, *roles[t], es) for t in ("gemm.qkv", "gemm.o", "gemm.gate_up", "gemm.down"))
     tot += L * int(np.sum(ctx)) * 2 * KVH * D * es  # context K/V read by attention
-    tot += M * H * es + V * H * es + B * K * H * es  # embedding rows, LM head, its input
+    tot += M * H * es + tag_bytes(spec, "gemm.lm_head", *roles["gemm.lm_head"], es)  # embedding rows, LM head
     tot += B * (2 * K + 1) * 4 * 2  # token ids in/out
     return tot
 
@@ -84,17 +101,17 @@ def source_sha(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM traffic per launch of the streaming GEMM from the committed rocprofv3 --pmc summary,
-    or None when absent or taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"gemm_stream_{workload}_pmc.json")
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc summary, or None
+    when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
     if d.get("source_sha") != source_sha(GEMM_SOURCES):
         return None
-    return d.get("traffic_bytes_per_launch")
+    return d.get("kernels", {}).get(kernel, {}).get("traffic_bytes_per_launch")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -259,13 +276,17 @@ def main():
     B, K = bench.B, spec.block_size - 1
     es = 2 if spec.dtype == "bf16" else 4
     roles = gemm_roles(spec, B * spec.block_size, B * wl.inject_rows)
-    launches_per_step = {t: (spec.n_layers if t in ("gemm.qkv", "gemm.o", "gemm.gate_up", "gemm.down") else 1)
-                         for t in roles}
-    g_bytes = sum(gemm_bytes(*roles[t], es) * launches_per_step[t] for t in STREAM_GEMM_TAGS) * args.steps
-    g_launch = sum(prof.get(t, (0, 0.0))[0] for t in STREAM_GEMM_TAGS)
-    g_ms = sum(prof.get(t, (0, 0.0))[1] for t in STREAM_GEMM_TAGS)
+    # dominant GEMM kernel of the step: the instance with the most event-timed time
+    per_kernel = {}
+    for kname, tags in GEMM_KERNELS.items():
+        n = sum(prof.get(t, (0, 0.0))[0] for t in tags)
+        ms = sum(prof.get(t, (0, 0.0))[1] for t in tags)
+        nbytes = sum(tag_bytes(spec, t, *roles[t], es) * prof.get(t, (0, 0.0))[0] for t in tags)
+        per_kernel[kname] = (n, ms, nbytes)
+    dom = max(per_kernel, key=lambda k: per_kernel[k][1])
+    g_launch, g_ms, g_bytes = per_kernel[dom]
     achieved = g_bytes / (g_ms * 1e-3) / 1e9 if g_ms > 0 else 0.0
-    traffic = load_traffic(wl.name)
+    traffic = load_traffic(dom, wl.name)
     sbytes = step_bytes(spec, B, bench.ctx, wl.inject_rows)
     result = {
         "metric": "drafted tokens/sec and draft blocks/sec (Qwen3-8B-shape, b16); % HBM/MFMA roofline",
@@ -289,12 +310,15 @@ def main():
         "ms_per_step_without_events": sec_plain * 1e3,
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": sbytes, "achieved": sbytes / sec / 1e9,
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": sbytes / sec / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "kernel": "gemm_kernel<bf16,MT=1,partial,one A segment> (weight streaming)",
+        "roofline": {"bound": "hbm", "kernel": dom,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "launches": g_launch,
                      "avg_launch_us": (g_ms / g_launch * 1e3) if g_launch else None,
                      "algorithmic_bytes_per_launch": g_bytes / g_launch if g_launch else None},
         "kernel_ms_per_step": {k: v[1] / args.steps for k, v in sorted(prof.items())},
+        "gemm_kernels": {k: {"launches_per_step": v[0] / args.steps, "ms_per_step": v[1] / args.steps,
+                             "achieved_GBs": v[2] / (v[1] * 1e-3) / 1e9 if v[1] else None}
+                         for k, v in per_kernel.items()},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(bench)

@@ -33,9 +33,9 @@ dflash_status ok() {
   return DFLASH_OK;
 }
 
-#define HIP_TRY(expr)                                                                      \
-  do {                                                                                     \
-    hipError_t e_ = (expr);                                                                \
+#define HIP_TRY(expr)                                                                          \
+  do {                                                                                         \
+    hipError_t e_ = (expr);                                                                    \
     if (e_ != hipSuccess) return fail(DFLASH_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
@@ -57,15 +57,19 @@ dflash_status check_config(const dflash_config *c) {
                 c->n_kv_heads);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(DFLASH_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", c->head_dim);
-  if (c->hidden % 64 || c->intermediate % 64 || (c->n_aux * c->target_hidden) % 64 || c->target_hidden % 32)
+  if (c->hidden % 128 || c->intermediate % 128 || (c->n_aux * c->target_hidden) % 128 || c->target_hidden % 32)
     return fail(DFLASH_ERR_UNSUPPORTED,
-                "hidden, intermediate and n_aux*target_hidden must be multiples of 64, target_hidden of 32");
+                "hidden, intermediate and n_aux*target_hidden must be multiples of 128, target_hidden of 32");
+  if ((c->n_q_heads * c->head_dim) % 128)
+    return fail(DFLASH_ERR_UNSUPPORTED, "n_q_heads * head_dim must be a multiple of 128");
+  if (c->hidden > 4096 * 4) return fail(DFLASH_ERR_UNSUPPORTED, "hidden %d above 16384", c->hidden);
   if (c->vocab % 16) return fail(DFLASH_ERR_UNSUPPORTED, "vocab %d is not a multiple of 16", c->vocab);
   if (c->block_size < 2 || c->block_size > 64)
     return fail(DFLASH_ERR_UNSUPPORTED, "block_size %d outside [2, 64]", c->block_size);
   if (c->block_size * (c->n_q_heads / c->n_kv_heads) > 64)
     return fail(DFLASH_ERR_UNSUPPORTED, "block_size * q-heads per kv-head exceeds 64");
   if (c->n_layers > 64) return fail(DFLASH_ERR_UNSUPPORTED, "more than 64 layers");
+  if (c->n_aux > 8) return fail(DFLASH_ERR_UNSUPPORTED, "more than 8 auxiliary layers");
   if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab)
     return fail(DFLASH_ERR_INVALID_ARGUMENT, "mask_token_id %d outside [0, vocab)", c->mask_token_id);
   if (!(c->rms_eps >= 0.f)) return fail(DFLASH_ERR_INVALID_ARGUMENT, "rms_eps must be >= 0");
@@ -95,9 +99,9 @@ InjectPlan plan_inject(const dflash_config *c, int rows) {
   p.rows = rows;
   const bool bf = is_bf16(c);
   const int kvn = c->n_layers * 2 * c->n_kv_heads * c->head_dim;
-  p.s_fc = gemm_plan_splits(rows, c->hidden, c->n_aux * c->target_hidden, bf);
-  p.s_kv = gemm_plan_splits(rows, kvn, c->hidden, bf);
-  const size_t part = std::max((size_t)p.s_fc * rows * c->hidden, (size_t)p.s_kv * rows * kvn) * sizeof(float);
+  p.s_fc = gemm_plan_splits(rows, c->hidden, c->n_aux * c->target_hidden, bf, GemmEpi::kStore);
+  p.s_kv = gemm_plan_splits(rows, std::max(kvn, 16), c->hidden, bf, GemmEpi::kStore);
+  const size_t part = std::max((size_t)p.s_fc * c->hidden, (size_t)p.s_kv * kvn) * rows * sizeof(float);
   Carver cv;
   p.off_part = cv.take(part);
   p.off_ctx = cv.take((size_t)rows * c->hidden * elem_size(c));
@@ -122,15 +126,16 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
   p.M = B * c->block_size;
   p.Mk = B * K;
   const int nqkv = (QH + 2 * KVH) * D;
-  p.s_qkv = gemm_plan_splits(p.M, nqkv, H, bf);
-  p.s_o = gemm_plan_splits(p.M, H, QH * D, bf);
-  p.s_gu = gemm_plan_splits(p.M, 2 * I, H, bf);
-  p.s_down = gemm_plan_splits(p.M, H, I, bf);
+  p.s_qkv = gemm_plan_splits(p.M, nqkv, H, bf, GemmEpi::kStore);
+  p.s_o = gemm_plan_splits(p.M, H, QH * D, bf, GemmEpi::kResidAdd);
+  p.s_gu = gemm_plan_splits(p.M, I, H, bf, GemmEpi::kSwiGLU);
+  p.s_down = gemm_plan_splits(p.M, H, I, bf, GemmEpi::kResidAdd);
   attn_plan(B, KVH, max_ctx + c->block_size, &p.chunk, &p.nsplit);
-  p.lm_groups = (c->vocab + 63) / 64;
+  p.lm_groups = gemm_col_groups(p.Mk, c->vocab, GemmEpi::kArgmax);
   const size_t es = elem_size(c);
-  const size_t part = std::max(std::max((size_t)p.s_qkv * nqkv, (size_t)p.s_o * H),
-                               std::max((size_t)p.s_gu * 2 * I, (size_t)p.s_down * H)) *
+  // partials: QKV always (its consumer is the q/k norm kernel); the others only when split
+  const size_t part = std::max(std::max((size_t)p.s_qkv * nqkv, (size_t)(p.s_o > 1 ? p.s_o : 0) * H),
+                               std::max((size_t)(p.s_gu > 1 ? p.s_gu : 0) * 2 * I, (size_t)(p.s_down > 1 ? p.s_down : 0) * H)) *
                       p.M * sizeof(float);
   Carver cv;
   p.off_x = cv.take((size_t)p.M * H * sizeof(float));
@@ -175,6 +180,19 @@ dflash_status check_cache(const dflash_config *c, const dflash_kv_cache *kv) {
   for (int l = 0; l < c->n_layers; ++l)
     if (!kv->k[l] || !kv->v[l]) return fail(DFLASH_ERR_INVALID_ARGUMENT, "cache of layer %d is NULL", l);
   return DFLASH_OK;
+}
+
+GemmArgs gemm_args(const char *tag, const void *a, int64_t lda, int M, int N, int K) {
+  GemmArgs g{};
+  g.a[0] = a;
+  g.a_nseg = 1;
+  g.lda = lda;
+  g.b_nseg = 1;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.tag = tag;
+  return g;
 }
 
 }  // namespace
@@ -259,8 +277,7 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
   if (aux_row_stride % vec) return fail(DFLASH_ERR_UNSUPPORTED, "aux_row_stride must be a multiple of %d", vec);
   if (!positions || !slot_mapping) return fail(DFLASH_ERR_INVALID_ARGUMENT, "positions or slot_mapping is NULL");
   if (!workspace) return fail(DFLASH_ERR_INVALID_ARGUMENT, "workspace is NULL");
-  if (cfg->n_aux > 8) return fail(DFLASH_ERR_UNSUPPORTED, "more than 8 auxiliary layers");
-  if (n_rows > 0 && cfg->n_layers == 0) return ok();  // nothing to write
+  if (cfg->n_layers == 0) return ok();  // nothing to write
 
   hipStream_t s = (hipStream_t)stream;
   const bool bf = is_bf16(cfg);
@@ -275,44 +292,32 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
     float *part = at<float>(workspace, p.off_part);
     void *ctx = at<char>(workspace, p.off_ctx);
 
-    GemmArgs g{};
+    // fc over the concatenated auxiliary states, read in place from the n_aux pointers
+    GemmArgs g = gemm_args("gemm.fc", nullptr, aux_row_stride, rows, H, cfg->n_aux * cfg->target_hidden);
     for (int j = 0; j < cfg->n_aux; ++j)
       g.a[j] = static_cast<const char *>(aux[j]) + (size_t)r0 * aux_row_stride * es;
     g.a_nseg = cfg->n_aux;
-    g.lda = aux_row_stride;
     g.b[0] = w->fc;
     g.b_end[0] = H;
-    g.b_nseg = 1;
-    g.M = rows;
-    g.N = H;
-    g.K = cfg->n_aux * cfg->target_hidden;
-    g.splits = p.s_fc;
+    g.out = part;
     g.part = part;
-    g.tag = "gemm.fc";
-    HIP_TRY(launch_gemm(g, bf, GemmEpi::kPartial, s));
+    HIP_TRY(launch_gemm(g, bf, GemmEpi::kStore, p.s_fc, s));
+    // hidden_norm
     HIP_TRY(launch_rmsnorm(bf, rows, H, nullptr, part, p.s_fc, w->hidden_norm, cfg->rms_eps, ctx, 0, nullptr, s));
-
-    GemmArgs k{};
-    k.a[0] = ctx;
-    k.a_nseg = 1;
-    k.lda = H;
+    // K/V of every layer in one projection
+    GemmArgs k = gemm_args("gemm.kv", ctx, H, rows, kvn, H);
     k.b[0] = w->kv_fused;
     k.b_end[0] = kvn;
-    k.b_nseg = 1;
-    k.M = rows;
-    k.N = kvn;
-    k.K = H;
-    k.splits = p.s_kv;
+    k.out = part;
     k.part = part;
-    k.tag = "gemm.kv";
-    HIP_TRY(launch_gemm(k, bf, GemmEpi::kPartial, s));
+    HIP_TRY(launch_gemm(k, bf, GemmEpi::kStore, p.s_kv, s));
 
     KvScatterArgs a{};
     a.N = rows;
     a.L = cfg->n_layers;
     a.KVH = cfg->n_kv_heads;
     a.D = cfg->head_dim;
-    a.part = part;
+    a.kv = part;
     a.splits = p.s_kv;
     for (int l = 0; l < cfg->n_layers; ++l) {
       a.k_norm[l] = w->k_norm[l];
@@ -344,7 +349,8 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
   if ((st = check_cache(cfg, cache)) != DFLASH_OK) return st;
   if (!cache->block_table || cache->max_blocks_per_seq <= 0)
     return fail(DFLASH_ERR_INVALID_ARGUMENT, "block_table is NULL or max_blocks_per_seq <= 0");
-  if (!w->embed || !w->lm_head || !w->final_norm) return fail(DFLASH_ERR_INVALID_ARGUMENT, "embed/lm_head/final_norm NULL");
+  if (!w->embed || !w->lm_head || !w->final_norm)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "embed/lm_head/final_norm NULL");
   const int L = cfg->n_layers;
   if (L > 0 && (!w->in_norm || !w->wq || !w->wk || !w->wv || !w->q_norm || !w->wo || !w->post_norm || !w->w_gate ||
                 !w->w_up || !w->w_down))
@@ -376,14 +382,12 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
   void *f = at<char>(workspace, p.off_f);
 
   HIP_TRY(launch_embed(bf, w->embed, cfg->vocab, H, bonus_tokens, batch, bs, cfg->mask_token_id, x, s));
-  int pending = 0;  // split count of the down-projection partials not yet added to x
+  int pending = 0;  // split count of down-projection partials not yet added to x
   for (int l = 0; l < L; ++l) {
     HIP_TRY(launch_rmsnorm(bf, M, H, x, part, pending, w->in_norm[l], cfg->rms_eps, h, 0, nullptr, s));
 
-    GemmArgs g{};
-    g.a[0] = h;
-    g.a_nseg = 1;
-    g.lda = H;
+    // q | k | v in one pass over the three projections
+    GemmArgs g = gemm_args("gemm.qkv", h, H, M, (QH + 2 * KVH) * D, H);
     g.b[0] = w->wq[l];
     g.b[1] = w->wk[l];
     g.b[2] = w->wv[l];
@@ -391,13 +395,9 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     g.b_end[1] = (QH + KVH) * D;
     g.b_end[2] = (QH + 2 * KVH) * D;
     g.b_nseg = 3;
-    g.M = M;
-    g.N = (QH + 2 * KVH) * D;
-    g.K = H;
-    g.splits = p.s_qkv;
+    g.out = part;
     g.part = part;
-    g.tag = "gemm.qkv";
-    HIP_TRY(launch_gemm(g, bf, GemmEpi::kPartial, s));
+    HIP_TRY(launch_gemm(g, bf, GemmEpi::kStore, p.s_qkv, s));
     HIP_TRY(launch_qk_norm_rope(bf, M, bs, QH, KVH, D, part, p.s_qkv, w->q_norm[l], w->k_norm[l], cfg->rms_eps,
                                 w->rope_cos, w->rope_sin, w->rope_max_pos, seq_lens, max_context, q, kb, vb, s));
 
@@ -426,74 +426,45 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     at_.o = o;
     HIP_TRY(launch_attention(bf, at_, s));
 
-    GemmArgs go{};
-    go.a[0] = o;
-    go.a_nseg = 1;
-    go.lda = QH * D;
+    // O projection: residual add in place, or split partials summed by the post-norm
+    GemmArgs go = gemm_args("gemm.o", o, QH * D, M, H, QH * D);
     go.b[0] = w->wo[l];
     go.b_end[0] = H;
-    go.b_nseg = 1;
-    go.M = M;
-    go.N = H;
-    go.K = QH * D;
-    go.splits = p.s_o;
+    go.out = x;
     go.part = part;
-    go.tag = "gemm.o";
-    HIP_TRY(launch_gemm(go, bf, GemmEpi::kPartial, s));
-    HIP_TRY(launch_rmsnorm(bf, M, H, x, part, p.s_o, w->post_norm[l], cfg->rms_eps, h, 0, nullptr, s));
+    HIP_TRY(launch_gemm(go, bf, GemmEpi::kResidAdd, p.s_o, s));
+    HIP_TRY(launch_rmsnorm(bf, M, H, x, part, p.s_o > 1 ? p.s_o : 0, w->post_norm[l], cfg->rms_eps, h, 0, nullptr,
+                           s));
 
-    GemmArgs gu{};
-    gu.a[0] = h;
-    gu.a_nseg = 1;
-    gu.lda = H;
+    // gate | up with SwiGLU (in place when unsplit)
+    GemmArgs gu = gemm_args("gemm.gate_up", h, H, M, I, H);
     gu.b[0] = w->w_gate[l];
     gu.b[1] = w->w_up[l];
     gu.b_end[0] = I;
-    gu.b_end[1] = 2 * I;
+    gu.b_end[1] = I;
     gu.b_nseg = 2;
-    gu.M = M;
-    gu.N = 2 * I;
-    gu.K = H;
-    gu.splits = p.s_gu;
+    gu.act = act;
     gu.part = part;
-    gu.tag = "gemm.gate_up";
-    HIP_TRY(launch_gemm(gu, bf, GemmEpi::kPartial, s));
-    HIP_TRY(launch_swiglu(bf, M, I, part, p.s_gu, act, s));
+    HIP_TRY(launch_gemm(gu, bf, GemmEpi::kSwiGLU, p.s_gu, s));
+    if (p.s_gu > 1) HIP_TRY(launch_swiglu(bf, M, I, part, p.s_gu, act, s));
 
-    GemmArgs gd{};
-    gd.a[0] = act;
-    gd.a_nseg = 1;
-    gd.lda = I;
+    GemmArgs gd = gemm_args("gemm.down", act, I, M, H, I);
     gd.b[0] = w->w_down[l];
     gd.b_end[0] = H;
-    gd.b_nseg = 1;
-    gd.M = M;
-    gd.N = H;
-    gd.K = I;
-    gd.splits = p.s_down;
+    gd.out = x;
     gd.part = part;
-    gd.tag = "gemm.down";
-    HIP_TRY(launch_gemm(gd, bf, GemmEpi::kPartial, s));
-    pending = p.s_down;
+    HIP_TRY(launch_gemm(gd, bf, GemmEpi::kResidAdd, p.s_down, s));
+    pending = p.s_down > 1 ? p.s_down : 0;
   }
   // final norm on the drafted rows (block slots 1..K), compacted to [B*K, H]
   HIP_TRY(launch_rmsnorm(bf, M, H, x, part, pending, w->final_norm, cfg->rms_eps, f, bs, hidden_out, s));
 
-  GemmArgs gl{};
-  gl.a[0] = f;
-  gl.a_nseg = 1;
-  gl.lda = H;
+  GemmArgs gl = gemm_args("gemm.lm_head", f, H, p.Mk, cfg->vocab, H);
   gl.b[0] = w->lm_head;
   gl.b_end[0] = cfg->vocab;
-  gl.b_nseg = 1;
-  gl.M = p.Mk;
-  gl.N = cfg->vocab;
-  gl.K = H;
-  gl.splits = 1;
-  gl.tag = "gemm.lm_head";
   gl.amax_val = at<float>(workspace, p.off_amv);
   gl.amax_idx = at<int32_t>(workspace, p.off_ami);
-  HIP_TRY(launch_gemm(gl, bf, GemmEpi::kArgmax, s));
+  HIP_TRY(launch_gemm(gl, bf, GemmEpi::kArgmax, 1, s));
   HIP_TRY(launch_argmax_reduce(batch, K, p.lm_groups, gl.amax_val, gl.amax_idx, bonus_tokens, cfg->vocab,
                                draft_token_ids, drafts_only, s));
   return ok();
@@ -503,7 +474,8 @@ dflash_status dflash_greedy_verify(int32_t batch, int32_t num_drafts, const int3
                                    const int32_t *target_tokens, int32_t *accepted_len, int32_t *output_tokens,
                                    int32_t *next_bonus, void *stream) {
   if (batch < 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "batch < 0");
-  if (num_drafts < 1 || num_drafts > 63) return fail(DFLASH_ERR_UNSUPPORTED, "num_drafts %d outside [1, 63]", num_drafts);
+  if (num_drafts < 1 || num_drafts > 63)
+    return fail(DFLASH_ERR_UNSUPPORTED, "num_drafts %d outside [1, 63]", num_drafts);
   if (batch == 0) return ok();
   if (!draft_tokens || !target_tokens || !accepted_len || !output_tokens || !next_bonus)
     return fail(DFLASH_ERR_INVALID_ARGUMENT, "an input/output pointer is NULL");

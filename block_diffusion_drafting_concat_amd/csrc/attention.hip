@@ -197,26 +197,48 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split partials of one (sequence, kv head, query row); one thread per element.
+// Merge the split partials of one (sequence, kv head, query row); one thread per element of
+// the head vector. The split weights exp2(m_s - max m) are computed once into LDS.
 template <typename T>
-__global__ void attn_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
+  extern __shared__ float wsplit[];  // [nsplit]
+  __shared__ float red[16];
   const int row = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.QH / a.KVH;
   const int D = a.D;
   const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
   const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64;
-  float mmax = -INFINITY;
-  for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, a.pm[base + s * 64 + row]);
+  float mloc = -INFINITY;
+  for (int s = threadIdx.x; s < ns; s += blockDim.x) mloc = fmaxf(mloc, a.pm[base + s * 64 + row]);
+  mloc = wave_max(mloc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mloc;
+  __syncthreads();
+  float mmax = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) mmax = fmaxf(mmax, red[i]);
+  __syncthreads();
+  float dloc = 0.f;
+  for (int s = threadIdx.x; s < ns; s += blockDim.x) {
+    const float wgt = exp2f(a.pm[base + s * 64 + row] - mmax);
+    wsplit[s] = wgt;
+    dloc += wgt * a.pl[base + s * 64 + row];
+  }
+  const float den = block_sum(dloc, red);  // synchronises, so wsplit is visible
   const int hh = row / a.bs, j = row % a.bs;
   T *o = reinterpret_cast<T *>(a.o) + ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float w = exp2f(a.pm[base + s * 64 + row] - mmax);
-      num += w * a.po[(base + s * 64 + row) * D + d];
-      den += w * a.pl[base + s * 64 + row];
+    const float *po = a.po + (base + row) * D + d;
+    float num = 0.f;
+    int s = 0;
+    for (; s + 4 <= ns; s += 4) {
+      const float p0 = po[(size_t)(s + 0) * 64 * D], p1 = po[(size_t)(s + 1) * 64 * D];
+      const float p2 = po[(size_t)(s + 2) * 64 * D], p3 = po[(size_t)(s + 3) * 64 * D];
+      num += wsplit[s] * p0;
+      num += wsplit[s + 1] * p1;
+      num += wsplit[s + 2] * p2;
+      num += wsplit[s + 3] * p3;
     }
+    for (; s < ns; ++s) num += wsplit[s] * po[(size_t)s * 64 * D];
     Storage<T>::store(o, d, num / den);
   }
 }
@@ -236,7 +258,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
   const int G = a.QH / a.KVH;
   {
     ProfScope prof("attn_merge", s);
-    attn_merge_kernel<T><<<dim3(a.bs * G, a.KVH, a.B), a.D, 0, s>>>(a);
+    attn_merge_kernel<T><<<dim3(a.bs * G, a.KVH, a.B), a.D, a.nsplit * sizeof(float), s>>>(a);
   }
   return hipGetLastError();
 }

@@ -1,174 +1,339 @@
 // Weight-streaming MFMA GEMM for the drafter's projections and the LM head.
 //
-// Every projection of the drafter is C = A W^T with a short activation A (the block's
-// rows: 16 at batch 1) and a long weight W [N, K] read once from HBM. The kernel is
-// organised around streaming W: each wave owns 16 output columns (16 rows of W) and walks
-// its K slice in 16-byte-per-lane loads that feed v_mfma_f32_16x16x32_bf16 directly (B
-// operand = 16 W rows x 64 contiguous bytes per instruction). Up to 64 activation rows are
-// held as MT accumulator tiles; larger M is covered by grid.z blocks of 64 rows. The K
-// range can be split over grid.y so that even narrow projections (N = 4096) put enough
-// waves on the 256 CUs to keep HBM busy; the split partials are summed in fixed order by
-// the consumer kernel (no float atomics, so results are deterministic).
+// Every projection of the drafter is C = A W^T with a short activation A (the block's rows:
+// 16 at batch 1) and a long weight W [N, K] that must be read once from HBM. The kernel is
+// organised around streaming W at full HBM rate:
+//  * a work-group owns 16*CW output columns and one K slice of the split-K grid (grid.y);
+//    its CW*KW waves are CW column tiles x KW sub-slices of K;
+//  * each wave streams its 16 W rows in 16-byte-per-lane loads that feed
+//    v_mfma_f32_16x16x32_bf16 directly (B operand = 16 W rows x 64 contiguous bytes), double
+//    buffered in registers; its first loads are issued before the activation staging so the
+//    HBM stream starts at once;
+//  * the activation slice is staged in LDS (in passes of at most kPassBytes), so A fragments
+//    come from LDS and the vector-memory path carries only weights;
+//  * the KW sub-slice tiles are summed through LDS in a fixed order. With one split the
+//    epilogue is applied in place (fp32 store, residual add, SwiGLU, or the LM head's
+//    (max, lowest index) per work-group); with several, fp32 partials [split][M][N] go to
+//    the workspace and the consumer kernel sums them in split order. There are no float
+//    atomics, so results are deterministic.
+// Up to 64 activation rows are held as MT accumulator tiles; more rows use grid.z blocks.
 #include "common.h"
 #include "kernels.h"
 
 namespace dflash {
 namespace {
 
-constexpr int kWaves = 4;   // waves per work-group; each owns 16 output columns
-constexpr int kUnroll = 4;  // 16-byte K steps in flight per lane per iteration
+constexpr int kPassBytes = 60 << 10;  // LDS budget of one staged A pass (+ padding < 64 KiB)
+constexpr int kGroup = 4;             // 16-byte K steps per register buffer
 
-template <typename T, int MT, bool kArgmax, bool kMultiA>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  constexpr int KPV = Storage<T>::kPerVec;  // K elements per lane per 16-byte load
-  constexpr int CH = 4 * KPV;               // K elements per wave step
+template <typename T>
+__host__ __device__ constexpr int ch_of() {
+  return 4 * Storage<T>::kPerVec;  // K elements per wave MFMA step
+}
+
+template <typename T, int MT, int CW, int KW, GemmEpi E, bool kMultiA>
+__global__ __launch_bounds__(CW *KW * 64) void gemm_kernel(GemmArgs g) {
+  constexpr int NW = CW * KW;
+  constexpr int KPV = Storage<T>::kPerVec;
+  constexpr int CH = ch_of<T>();
+  constexpr bool kDual = E == GemmEpi::kSwiGLU;
+  constexpr int NACC = kDual ? 2 : 1;
+  constexpr int U = kGroup;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T *sa = reinterpret_cast<T *>(smem);
+  float *red = reinterpret_cast<float *>(smem);
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x * kWaves + wave) * 16;
-  const int m_base = blockIdx.z * (16 * MT);
-  const int ks = (g.K / g.splits + CH - 1) / CH * CH;  // K per split, a multiple of CH
-  const int kb = blockIdx.y * ks;
-  const int ke = min(g.K, kb + ks);
-  const bool active = n0 < g.N;
+  const int cw = wave % CW, kw = wave / CW;
+  const int n0 = blockIdx.x * 16 * CW;
+  const int ncol = n0 + cw * 16;
+  const int m0 = blockIdx.z * 16 * MT;
+  const int kb = blockIdx.y * g.kt;
+  const int ke = min(g.K, kb + g.kt);
+  const int kp = g.kp;      // K per staged pass (multiple of KW * CH)
+  const int as = kp + KPV;  // LDS row stride of the A pass (16-byte pad)
+  const int kq = kp / KW;   // K per wave per pass
+  const bool active = ncol < g.N;
+  const int kg = (lane >> 4) * KPV;
+  const int a_seglen = g.K / g.a_nseg;
 
-  f32x4_t acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  if (active) {
-    // this wave's 16 W rows
+  const T *brow[NACC];
+  {
     int seg = 0, nbase = 0;
-    while (seg < g.b_nseg - 1 && n0 >= g.b_end[seg]) nbase = g.b_end[seg++];
-    const T *brow = reinterpret_cast<const T *>(g.b[seg]) + (size_t)(n0 - nbase + (lane & 15)) * g.K;
-    const int kg = (lane >> 4) * KPV;
-    const int a_seglen = g.K / g.a_nseg;
-    bool mvalid[MT];
-    size_t aoff[MT];
+    if (!kDual)
+      while (seg < g.b_nseg - 1 && ncol >= g.b_end[seg]) nbase = g.b_end[seg++];
+    const int r = active ? ncol - nbase + (lane & 15) : 0;
+    brow[0] = reinterpret_cast<const T *>(g.b[seg]) + (size_t)r * g.K + kg;
+    if (kDual) brow[NACC - 1] = reinterpret_cast<const T *>(g.b[1]) + (size_t)r * g.K + kg;
+  }
+
+  f32x4_t acc[NACC][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int m = m_base + t * 16 + (lane & 15);
-      mvalid[t] = m < g.M;
-      aoff[t] = (size_t)(mvalid[t] ? m : 0) * g.lda;
-    }
-    auto a_ptr = [&](int k) -> const T * {
-      if (kMultiA) {
-        const int s = k / a_seglen;
-        return reinterpret_cast<const T *>(g.a[s]) + (k - s * a_seglen);
+  for (int a = 0; a < NACC; ++a)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // The loads below are issued unconditionally (addresses clamped into the operand) so that
+  // the compiler can count outstanding loads exactly: weight loads stay in flight across the
+  // A staging and across each MFMA group (register double buffering).
+  const int vrow = kp / KPV;  // 16-byte vectors per staged A row
+  constexpr int NA = (kPassBytes / 16 + NW * 64 - 1) / (NW * 64);  // A vectors per thread, max
+  for (int p0 = kb; p0 < ke; p0 += kp) {
+    const int plen = min(kp, ke - p0);  // a multiple of CH
+    const int q0 = kw * kq;
+    const int q1 = min(plen, q0 + kq);
+    const int nsteps = active && q1 > q0 ? (q1 - q0) / CH : 0;
+    const int nfull = nsteps / U;
+    const int total = 16 * MT * vrow;  // A vectors of this pass
+    auto kclamp = [&](int st) { return p0 + min(q0 + st * CH, plen - CH); };
+    auto load_group = [&](Vec16 (&b)[NACC][U], int gi) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) b[a][u] = load_vec16(brow[a] + kclamp(gi * U + u));
+    };
+    auto compute = [&](const Vec16 (&b)[NACC][U], int st0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = q0 + (st0 + u) * CH;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          Vec16 af;
+          af.u = *reinterpret_cast<const uint4 *>(sa + (t * 16 + (lane & 15)) * as + k + kg);
+#pragma unroll
+          for (int a = 0; a < NACC; ++a) mma16<T>(acc[a][t], af, b[a][u]);
+        }
       }
-      return reinterpret_cast<const T *>(g.a[0]) + k;
     };
 
-    int k = kb;
-    for (; k + CH * kUnroll <= ke; k += CH * kUnroll) {
-      Vec16 bf[kUnroll];
-      Vec16 af[MT][kUnroll];
+    // ---- A rows [m0, m0 + 16*MT) x K [p0, p0 + plen): loads first, then weights group 0
+    Vec16 areg[NA];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) bf[u] = load_vec16(brow + k + u * CH + kg);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const T *ap = a_ptr(k + u * CH + kg);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) af[t][u] = mvalid[t] ? load_vec16(ap + aoff[t]) : zero_vec16();
+    for (int j = 0; j < NA; ++j) {
+      const int v = min((int)threadIdx.x + j * NW * 64, total - 1);
+      const int r = v / vrow, cv = v % vrow;
+      const int m = min(m0 + r, g.M - 1);
+      const int k = p0 + min(cv * KPV, plen - KPV);
+      const T *ap;
+      if (kMultiA) {
+        const int s = k / a_seglen;
+        ap = reinterpret_cast<const T *>(g.a[s]) + (k - s * a_seglen);
+      } else {
+        ap = reinterpret_cast<const T *>(g.a[0]) + k;
       }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) mma16<T>(acc[t], af[t][u], bf[u]);
+      areg[j] = load_vec16(ap + (size_t)m * g.lda);
     }
-    for (; k < ke; k += CH) {
-      const Vec16 bfv = load_vec16(brow + k + kg);
-      const T *ap = a_ptr(k + kg);
+    Vec16 b0[NACC][U], b1[NACC][U];
+    load_group(b0, 0);
+    __syncthreads();  // the previous pass has finished reading LDS
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int v = (int)threadIdx.x + j * NW * 64;
+      if (v < total) {
+        const int r = v / vrow, cv = v % vrow;
+        const bool ok = m0 + r < g.M && cv * KPV < plen;
+        *reinterpret_cast<uint4 *>(sa + r * as + cv * KPV) = ok ? areg[j].u : make_uint4(0, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+
+    // ---- stream this wave's K range of the pass: ping-pong register buffers, so one group
+    //      of weight loads is always in flight while the previous group feeds the MFMAs
+    int gi = 0;
+    for (; gi + 2 < nfull; gi += 2) {
+      load_group(b1, gi + 1);
+      compute(b0, gi * U);
+      load_group(b0, gi + 2);
+      compute(b1, (gi + 1) * U);
+    }
+    if (gi + 1 < nfull) {
+      load_group(b1, gi + 1);
+      compute(b0, gi * U);
+      compute(b1, (gi + 1) * U);
+    } else if (gi < nfull) {
+      compute(b0, gi * U);
+    }
+    for (int st = nfull * U; st < nsteps; ++st) {
+      const int k = q0 + st * CH;
+      Vec16 bf[NACC];
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) bf[a] = load_vec16(brow[a] + p0 + k);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        const Vec16 afv = mvalid[t] ? load_vec16(ap + aoff[t]) : zero_vec16();
-        mma16<T>(acc[t], afv, bfv);
+        Vec16 af;
+        af.u = *reinterpret_cast<const uint4 *>(sa + (t * 16 + (lane & 15)) * as + k + kg);
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) mma16<T>(acc[a][t], af, bf[a]);
       }
     }
   }
 
-  // Output tile layout: lane holds rows (lane/16)*4 + i, column lane%16.
-  const int col = n0 + (lane & 15);
-  if (!kArgmax) {
-    if (!active) return;
-    float *out = g.part + (size_t)blockIdx.y * g.M * g.N;
+  // ---- sum the KW sub-slice tiles in a fixed order, one row tile at a time. Tile layout:
+  //      lane holds rows (lane/16)*4 + i, column lane%16, stored at [lane*4 + i].
+  const bool direct = gridDim.y == 1;
+  float *fin = red + NW * NACC * 256;  // argmax: final logits [MT][CW][256]
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+  for (int t = 0; t < MT; ++t) {
+    __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m_base + t * 16 + (lane >> 4) * 4 + i;
-        if (m < g.M) out[(size_t)m * g.N + col] = acc[t][i];
+    for (int a = 0; a < NACC; ++a) *reinterpret_cast<f32x4_t *>(&red[(wave * NACC + a) * 256 + lane * 4]) = acc[a][t];
+    __syncthreads();
+    for (int e = threadIdx.x; e < CW * 256; e += NW * 64) {
+      const int c = e / 256, li = e % 256;
+      const int l = li >> 2, i = li & 3;
+      const int m = m0 + t * 16 + (l >> 4) * 4 + i;
+      const int col = n0 + c * 16 + (l & 15);
+      float v[NACC];
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < KW; ++q) sum += red[((q * CW + c) * NACC + a) * 256 + li];
+        v[a] = sum;
       }
-    return;
-  }
-
-  // Argmax over this work-group's 64 columns for each of its rows.
-  __shared__ float sv[kWaves][16 * MT];
-  __shared__ int si[kWaves][16 * MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = active ? acc[t][i] : -INFINITY;
-      int idx = active ? col : 0x7fffffff;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float ov = __shfl_xor(v, o, 64);
-        const int oi = __shfl_xor(idx, o, 64);
-        argmax_merge(v, idx, ov, oi);
+      if constexpr (E == GemmEpi::kArgmax) {
+        fin[(t * CW + c) * 256 + li] = (m < g.M && col < g.N) ? v[0] : -INFINITY;
+        continue;
       }
-      if ((lane & 15) == 0) {
-        sv[wave][t * 16 + (lane >> 4) * 4 + i] = v;
-        si[wave][t * 16 + (lane >> 4) * 4 + i] = idx;
+      if (m >= g.M || col >= g.N) continue;
+      const size_t o = (size_t)m * g.N + col;
+      if (!direct) {
+        float *part = g.part + (size_t)blockIdx.y * g.M * g.N * NACC;
+        if (kDual) {
+          part[(size_t)m * 2 * g.N + col] = v[0];
+          part[(size_t)m * 2 * g.N + g.N + col] = v[NACC - 1];
+        } else {
+          part[o] = v[0];
+        }
+      } else if constexpr (E == GemmEpi::kStore) {
+        g.out[o] = v[0];
+      } else if constexpr (E == GemmEpi::kResidAdd) {
+        g.out[o] += v[0];
+      } else if constexpr (E == GemmEpi::kSwiGLU) {
+        const float silu = v[0] / (1.f + expf(-v[0]));
+        Storage<T>::store(reinterpret_cast<T *>(g.act), o, silu * v[NACC - 1]);
       }
     }
-  __syncthreads();
-  if (threadIdx.x < 16 * MT) {
-    const int r = threadIdx.x;
-    float v = sv[0][r];
-    int idx = si[0][r];
-    for (int w = 1; w < kWaves; ++w) argmax_merge(v, idx, sv[w][r], si[w][r]);
-    const int m = m_base + r;
-    if (m < g.M) {
-      g.amax_val[(size_t)blockIdx.x * g.M + m] = v;
-      g.amax_idx[(size_t)blockIdx.x * g.M + m] = idx;
+  }
+  if constexpr (E == GemmEpi::kArgmax) {
+    // TPR threads per row scan the row's 16*CW columns, then a shuffle reduction
+    constexpr int TPR0 = NW * 64 / (16 * MT);
+    constexpr int TPR = TPR0 >= 32 ? 32 : TPR0 >= 16 ? 16 : TPR0 >= 8 ? 8 : TPR0 >= 4 ? 4 : TPR0 >= 2 ? 2 : 1;
+    __syncthreads();
+    if (threadIdx.x < 16 * MT * TPR) {
+      const int r = threadIdx.x / TPR, sub = threadIdx.x % TPR;
+      const int t = r / 16, rr = r % 16;
+      float best = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int j = sub; j < 16 * CW; j += TPR) {
+        const int c = j / 16, jj = j % 16;
+        argmax_merge(best, bi, fin[(t * CW + c) * 256 + ((rr / 4) * 16 + jj) * 4 + rr % 4], n0 + j);
+      }
+#pragma unroll
+      for (int o = TPR / 2; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        argmax_merge(best, bi, ov, oi);
+      }
+      const int m = m0 + r;
+      if (sub == 0 && m < g.M) {
+        g.amax_val[(size_t)m * gridDim.x + blockIdx.x] = best;
+        g.amax_idx[(size_t)m * gridDim.x + blockIdx.x] = bi;
+      }
     }
   }
 }
 
-template <typename T, bool kArgmax, bool kMultiA>
-hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
-  const int mt = g.M >= 64 ? 4 : (g.M + 15) / 16;
-  dim3 grid((g.N + 16 * kWaves - 1) / (16 * kWaves), g.splits, (g.M + 63) / 64);
-  if (g.M < 64) grid.z = 1;
-  switch (mt) {
-    case 1: gemm_kernel<T, 1, kArgmax, kMultiA><<<grid, 256, 0, s>>>(g); break;
-    case 2: gemm_kernel<T, 2, kArgmax, kMultiA><<<grid, 256, 0, s>>>(g); break;
-    case 3: gemm_kernel<T, 3, kArgmax, kMultiA><<<grid, 256, 0, s>>>(g); break;
-    default: gemm_kernel<T, 4, kArgmax, kMultiA><<<grid, 256, 0, s>>>(g); break;
-  }
+// Work-group shape (CW column tiles x KW K sub-slices) for a problem.
+struct Shape {
+  int cw, kw;
+};
+Shape pick_shape(int M, GemmEpi epi) {
+  if (gemm_mt(M) > 1) return {2, 2};
+  if (epi == GemmEpi::kArgmax) return {8, 1};
+  return {4, 2};
+}
+
+template <typename T, int MT, int CW, int KW, GemmEpi E>
+size_t lds_bytes(const GemmArgs &g) {
+  constexpr int KPV = Storage<T>::kPerVec;
+  const size_t a = (size_t)16 * MT * (g.kp + KPV) * sizeof(T);
+  const int nacc = E == GemmEpi::kSwiGLU ? 2 : 1;
+  size_t r = (size_t)CW * KW * nacc * 256 * sizeof(float);
+  if (E == GemmEpi::kArgmax) r += (size_t)CW * MT * 256 * sizeof(float);
+  return a > r ? a : r;
+}
+
+template <typename T, int MT, int CW, int KW, GemmEpi E, bool kMultiA>
+hipError_t launch_k(const GemmArgs &g, int splits, hipStream_t s) {
+  dim3 grid((g.N + 16 * CW - 1) / (16 * CW), splits, (g.M + 16 * MT - 1) / (16 * MT));
+  gemm_kernel<T, MT, CW, KW, E, kMultiA><<<grid, CW * KW * 64, lds_bytes<T, MT, CW, KW, E>(g), s>>>(g);
   return hipGetLastError();
 }
 
+template <typename T, GemmEpi E, bool kMultiA>
+hipError_t launch_t(const GemmArgs &g, int splits, hipStream_t s) {
+  switch (gemm_mt(g.M)) {
+    case 1:
+      if constexpr (E == GemmEpi::kArgmax) return launch_k<T, 1, 8, 1, E, kMultiA>(g, splits, s);
+      else return launch_k<T, 1, 4, 2, E, kMultiA>(g, splits, s);
+    case 2: return launch_k<T, 2, 2, 2, E, kMultiA>(g, splits, s);
+    case 3: return launch_k<T, 3, 2, 2, E, kMultiA>(g, splits, s);
+    default: return launch_k<T, 4, 2, 2, E, kMultiA>(g, splits, s);
+  }
+}
+
 template <typename T>
-hipError_t launch_dt(const GemmArgs &g, GemmEpi epi, hipStream_t s) {
+hipError_t launch_dt(const GemmArgs &g, GemmEpi epi, int splits, hipStream_t s) {
   const bool multi = g.a_nseg > 1;
-  if (epi == GemmEpi::kArgmax) return multi ? launch_t<T, true, true>(g, s) : launch_t<T, true, false>(g, s);
-  return multi ? launch_t<T, false, true>(g, s) : launch_t<T, false, false>(g, s);
+  switch (epi) {
+    case GemmEpi::kStore:
+      return multi ? launch_t<T, GemmEpi::kStore, true>(g, splits, s) : launch_t<T, GemmEpi::kStore, false>(g, splits, s);
+    case GemmEpi::kResidAdd: return launch_t<T, GemmEpi::kResidAdd, false>(g, splits, s);
+    case GemmEpi::kSwiGLU: return launch_t<T, GemmEpi::kSwiGLU, false>(g, splits, s);
+    default: return launch_t<T, GemmEpi::kArgmax, false>(g, splits, s);
+  }
+}
+
+int kstep(int M, GemmEpi epi, bool bf16) {
+  return pick_shape(M, epi).kw * (bf16 ? ch_of<uint16_t>() : ch_of<float>());
 }
 
 }  // namespace
 
-int gemm_plan_splits(int M, int N, int K, bool bf16) {
-  const int ch = bf16 ? 32 : 16;
-  const long waves = (long)((N + 15) / 16) * ((M + 63) / 64);
+int gemm_mt(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 48 ? 3 : 4; }
+
+int gemm_col_groups(int M, int N, GemmEpi epi) {
+  const int cols = 16 * pick_shape(M, epi).cw;
+  return (N + cols - 1) / cols;
+}
+
+int gemm_plan_splits(int M, int N, int K, bool bf16, GemmEpi epi) {
+  if (epi == GemmEpi::kArgmax) return 1;
+  const int step = kstep(M, epi, bf16);
+  const long wgs = (long)gemm_col_groups(M, N, epi) * ((M + 16 * gemm_mt(M) - 1) / (16 * gemm_mt(M)));
   int s = 1;
-  // Aim for >= 2048 streaming waves (8 per CU) while keeping >= 512 K per split.
-  while (waves * s < 2048 && K / (2 * s) >= 512 && (K / (2 * s)) % ch == 0 && s < 64) s *= 2;
+  // Up to ~1024 work-groups (4 per CU) while each split keeps >= 256 K and divides K.
+  while (wgs * s * 2 <= 1024 && K % (2 * s * step) == 0 && K / (2 * s) >= 256 && s < 64) s *= 2;
   return s;
 }
 
-hipError_t launch_gemm(const GemmArgs &g, bool bf16, GemmEpi epi, hipStream_t s) {
-  ProfScope prof(g.tag ? g.tag : "gemm", s);
-  return bf16 ? launch_dt<uint16_t>(g, epi, s) : launch_dt<float>(g, epi, s);
+hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, int splits, hipStream_t s) {
+  ProfScope prof(g0.tag ? g0.tag : "gemm", s);
+  const int step = kstep(g0.M, epi, bf16);
+  if ((epi != GemmEpi::kStore && g0.a_nseg > 1) || g0.N % 16 || g0.K % step || splits < 1 || g0.K % splits ||
+      (g0.K / splits) % step || (epi == GemmEpi::kArgmax && splits != 1) ||
+      (g0.a_nseg > 1 && (g0.K / g0.a_nseg) % (bf16 ? 8 : 4)))
+    return hipErrorInvalidValue;
+  GemmArgs g = g0;
+  g.kt = g.K / splits;
+  // K per staged pass: the split cut into equal passes that fit the LDS budget
+  const int mt = gemm_mt(g.M);
+  const int esz = bf16 ? 2 : 4;
+  const int kp_max = kPassBytes / (16 * mt * esz) / step * step;
+  const int npass = (g.kt + kp_max - 1) / kp_max;
+  g.kp = ((g.kt + npass - 1) / npass + step - 1) / step * step;
+  return bf16 ? launch_dt<uint16_t>(g, epi, splits, s) : launch_dt<float>(g, epi, splits, s);
 }
 
 }  // namespace dflash

@@ -12,12 +12,19 @@ namespace dflash {
 
 // ------------------------------------------------------------------------------------------
 // GEMM: C[m, n] = sum_k A[m, k] * B[n, k], A and B of the storage type, fp32 accumulation.
+// With one K split the epilogue is applied in the same kernel:
+//   kStore    out[m][n] = C                                   (fp32)
+//   kResidAdd out[m][n] += C                                  (the fp32 residual stream)
+//   kSwiGLU   act[m][n] = round(silu(C_gate) * C_up), B = {gate [N,K], up [N,K]}
+//   kArgmax   amax_{val,idx}[m][g] = (max, lowest index) over column group g (one split only)
+// With `splits` > 1 every split writes fp32 partials part[s][m][N] (SwiGLU: part[s][m][2N],
+// gate then up) and the consumer kernel sums them in split order.
 // A may be split along K into `a_nseg` equal segments with their own base pointers (the
-// auxiliary states of injection); B may be split along N into up to 3 matrices (q|k|v,
-// gate|up). The K range is divided into `splits` slices; slice s writes its partial sums to
-// part[s][m][n] (fp32). The argmax form instead writes, for every 64-column group and row,
-// the (max, lowest index) pair of the full-K logits.
+// auxiliary states of injection; kStore only); B may be split along N into up to 3
+// matrices (q|k|v). N must be a multiple of 16.
 // ------------------------------------------------------------------------------------------
+enum class GemmEpi { kStore, kResidAdd, kSwiGLU, kArgmax };
+
 struct GemmArgs {
   const void *a[8];
   int a_nseg;
@@ -26,18 +33,20 @@ struct GemmArgs {
   int b_end[3];  // exclusive N end of each B segment (b_end[nseg-1] == N)
   int b_nseg;
   int M, N, K;
-  int splits;
-  float *part;        // [splits][M][N]
-  float *amax_val;    // [ceil(N/64)][M]
-  int32_t *amax_idx;  // [ceil(N/64)][M]
+  float *out;         // kStore / kResidAdd: [M][N]
+  void *act;          // kSwiGLU: [M][N] of the storage type
+  float *part;        // splits > 1: [splits][M][N] (SwiGLU [splits][M][2N])
+  float *amax_val;    // kArgmax: [M][gemm_col_groups(N)]
+  int32_t *amax_idx;  // kArgmax: [M][gemm_col_groups(N)]
   const char *tag;    // name under which the launch is timed when profiling is on
+  int kt, kp;         // set by launch_gemm: K per split, K per staged LDS pass
 };
 
-enum class GemmEpi { kPartial, kArgmax };
-
-// The split count and K slice used for a (M, N, K) problem; shared by planning and launch.
-int gemm_plan_splits(int M, int N, int K, bool bf16);
-hipError_t launch_gemm(const GemmArgs &g, bool bf16, GemmEpi epi, hipStream_t s);
+int gemm_mt(int M);
+int gemm_col_groups(int M, int N, GemmEpi epi);  // work-group column groups (argmax groups)
+// Split count for a (M, N, K) problem; shared by workspace planning and launch.
+int gemm_plan_splits(int M, int N, int K, bool bf16, GemmEpi epi);
+hipError_t launch_gemm(const GemmArgs &g, bool bf16, GemmEpi epi, int splits, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------
 // Row-wise kernels
@@ -46,27 +55,30 @@ hipError_t launch_gemm(const GemmArgs &g, bool bf16, GemmEpi epi, hipStream_t s)
 hipError_t launch_embed(bool bf16, const void *embed, int V, int H, const int32_t *bonus,
                         int B, int bs, int mask_id, float *x, hipStream_t s);
 
-// For each row m: r = (resid ? resid[m] : 0) + sum_s part[s][m] ; if resid, resid[m] = r;
-// out[row_map(m)] = round(rmsnorm(r) * w). With keep_bs > 0 only rows with m % keep_bs != 0
-// are normalised, and they are written compactly (block slot 0 dropped): out row
-// (m / keep_bs) * (keep_bs - 1) + m % keep_bs - 1. hidden_out (optional) gets the same rows.
-hipError_t launch_rmsnorm(bool bf16, int M, int H, float *resid, const float *part, int splits,
+// For each row m: r = (x ? x[m] : 0) + sum_s part[s][m] (split order); if x and splits,
+// x[m] = r; out[row_map(m)] = round(rmsnorm(r) * w). With keep_bs > 0 only rows with
+// m % keep_bs != 0 are normalised, and they are written compactly (block slot 0 dropped):
+// out row (m / keep_bs) * (keep_bs - 1) + m % keep_bs - 1. hidden_out (optional) gets the
+// same rows.
+hipError_t launch_rmsnorm(bool bf16, int M, int H, float *x, const float *part, int splits,
                           const void *w, float eps, void *out, int keep_bs, void *hidden_out,
                           hipStream_t s);
 
-// q/k/v of the block: sum the QKV partials, per-head RMSNorm + RoPE on q and k (position
-// seq_lens[b] + j), round; writes q [M][QH][D], k and v [M][KVH][D].
-hipError_t launch_qk_norm_rope(bool bf16, int M, int bs, int QH, int KVH, int D, const float *part,
+// q/k/v of the block from the fp32 QKV projection partials [splits][M][(QH+2KVH)*D]: per-head
+// RMSNorm + RoPE on q and k (position seq_lens[b] + j), round; writes q [M][QH][D], k and v
+// [M][KVH][D].
+hipError_t launch_qk_norm_rope(bool bf16, int M, int bs, int QH, int KVH, int D, const float *qkv,
                                int splits, const void *q_norm, const void *k_norm, float eps,
                                const float *rope_cos, const float *rope_sin, int rope_max_pos,
                                const int32_t *seq_lens, int max_ctx, void *q, void *k, void *v,
                                hipStream_t s);
 
-// Context K/V of injection: sum the fused-KV partials [splits][N][L*2*KVH*D], k_norm + RoPE
-// on keys, round, scatter both to slot_mapping[r] of every layer's cache.
+// Context K/V of injection from the fp32 fused-KV projection partials
+// [splits][N][L*2*KVH*D]: k_norm + RoPE on keys, round, scatter both to slot_mapping[r] of
+// every layer's cache.
 struct KvScatterArgs {
   int N, L, KVH, D;
-  const float *part;
+  const float *kv;
   int splits;
   const void *k_norm[64];
   float eps;
@@ -80,11 +92,12 @@ struct KvScatterArgs {
 };
 hipError_t launch_kv_scatter(bool bf16, const KvScatterArgs &a, hipStream_t s);
 
-// act[m][n] = round(silu(sum_s part[s][m][n]) * sum_s part[s][m][I + n]).
+// act[m][n] = round(silu(sum_s part[s][m][n]) * sum_s part[s][m][I + n]), part [splits][M][2I].
 hipError_t launch_swiglu(bool bf16, int M, int I, const float *part, int splits, void *act,
                          hipStream_t s);
 
-// Final argmax over the 64-column groups and output assembly.
+// Final argmax over the column groups val/idx [B*K][ngroups] (lowest index on ties) and
+// output assembly.
 hipError_t launch_argmax_reduce(int B, int K, int ngroups, const float *val, const int32_t *idx,
                                 const int32_t *bonus, int V, int32_t *draft_ids,
                                 int32_t *drafts_only, hipStream_t s);

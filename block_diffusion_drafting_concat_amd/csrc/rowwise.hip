@@ -1,8 +1,13 @@
 // Row-wise kernels of the DFlash path: block embedding, RMSNorm (with the split-K partial
-// sum and residual add folded in), q/k RMSNorm + RoPE of the block, the context K/V
+// sum and the residual add folded in), q/k RMSNorm + RoPE of the block, the context K/V
 // epilogue of injection (k_norm + RoPE + paged scatter), SwiGLU, the LM-head argmax
 // reduction, greedy verification and the RoPE table.
+//
+// Every consumer of split-K GEMM partials sums them in split order, so results do not
+// depend on scheduling.
 #include <float.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "kernels.h"
@@ -14,42 +19,78 @@ namespace {
 // Block construction + embedding: row m = b*bs + j gets embed[bonus[b]] for j == 0 and
 // embed[mask] otherwise, converted to the fp32 residual stream.
 template <typename T>
-__global__ void embed_kernel(const T *embed, int V, int H, const int32_t *bonus, int bs, int mask_id,
-                             float *x) {
+__global__ __launch_bounds__(256) void embed_kernel(const T *__restrict__ embed, int V, int H,
+                                                    const int32_t *__restrict__ bonus, int bs, int mask_id,
+                                                    float *__restrict__ x) {
   const int m = blockIdx.x;
   const int b = m / bs, j = m % bs;
   int id = (j == 0) ? bonus[b] : mask_id;
   id = min(max(id, 0), V - 1);
   const T *src = embed + (size_t)id * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) x[(size_t)m * H + i] = Storage<T>::load(src, i);
+  for (int i = threadIdx.x * 4; i < H; i += blockDim.x * 4) {
+    float4 v;
+    v.x = Storage<T>::load(src, i);
+    v.y = Storage<T>::load(src, i + 1);
+    v.z = Storage<T>::load(src, i + 2);
+    v.w = Storage<T>::load(src, i + 3);
+    *reinterpret_cast<float4 *>(x + (size_t)m * H + i) = v;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
-// r = resid[m] + sum_s part[s][m]; resid[m] = r; out = round(r / rms(r) * w).
+// r = (x[m] or 0) + sum_s part[s][m]; x[m] = r; out = round(r / rms(r) * w). One work-group
+// of up to 1024 threads per row; each thread owns at most kRmsVecs float4 of the row and
+// the split loop is unrolled so that the partials stream in parallel.
+constexpr int kRmsVecs = 4;
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(int M, int H, float *resid, const float *part,
-                                                      int splits, const T *w, float eps, T *out,
-                                                      int keep_bs, T *hidden_out) {
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(int M, int H, float *__restrict__ x,
+                                                      const float *__restrict__ part, int splits,
+                                                      const T *__restrict__ w, float eps, T *__restrict__ out,
+                                                      int keep_bs, T *__restrict__ hidden_out) {
   __shared__ float red[16];
-  extern __shared__ float row[];
   const int m = blockIdx.x;
   if (keep_bs > 0 && m % keep_bs == 0) return;  // block slot 0 is not drafted
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    float v = resid ? resid[(size_t)m * H + i] : 0.f;
-    for (int s = 0; s < splits; ++s) v += part[((size_t)s * M + m) * H + i];
-    row[i] = v;
-    ss += v * v;
+  const int nv = H / 4;
+  float4 v[kRmsVecs];
+#pragma unroll
+  for (int j = 0; j < kRmsVecs; ++j) {
+    const int i = threadIdx.x + j * (int)blockDim.x;
+    v[j] = (x && i < nv) ? reinterpret_cast<const float4 *>(x + (size_t)m * H)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+#pragma unroll 4
+  for (int s = 0; s < splits; ++s) {
+    const float4 *p = reinterpret_cast<const float4 *>(part + ((size_t)s * M + m) * H);
+#pragma unroll
+    for (int j = 0; j < kRmsVecs; ++j) {
+      const int i = threadIdx.x + j * (int)blockDim.x;
+      if (i < nv) {
+        const float4 q = p[i];
+        v[j].x += q.x;
+        v[j].y += q.y;
+        v[j].z += q.z;
+        v[j].w += q.w;
+      }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kRmsVecs; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
   ss = block_sum(ss, red);
   const float inv = rsqrtf(ss / (float)H + eps);
   const int orow = keep_bs > 0 ? (m / keep_bs) * (keep_bs - 1) + m % keep_bs - 1 : m;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    const float v = row[i];
-    if (resid && splits > 0) resid[(size_t)m * H + i] = v;
-    const float y = v * inv * Storage<T>::load(w, i);
-    Storage<T>::store(out, (size_t)orow * H + i, y);
-    if (hidden_out) Storage<T>::store(hidden_out, (size_t)orow * H + i, y);
+#pragma unroll
+  for (int j = 0; j < kRmsVecs; ++j) {
+    const int i = threadIdx.x + j * (int)blockDim.x;
+    if (i >= nv) break;
+    if (x && splits > 0) reinterpret_cast<float4 *>(x + (size_t)m * H)[i] = v[j];
+    const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const size_t col = (size_t)i * 4 + c;
+      const float y = e[c] * inv * Storage<T>::load(w, col);
+      Storage<T>::store(out, (size_t)orow * H + col, y);
+      if (hidden_out) Storage<T>::store(hidden_out, (size_t)orow * H + col, y);
+    }
   }
 }
 
@@ -68,11 +109,13 @@ __device__ __forceinline__ void norm_rope_pair(float &x1, float &x2, bool own, i
 // One wave per (row, head). Heads [0, QH) are q, [QH, QH+KVH) k, then v.
 template <typename T>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(int M, int bs, int QH, int KVH, int D,
-                                                           const float *part, int splits, const T *q_norm,
-                                                           const T *k_norm, float eps, const float *rope_cos,
-                                                           const float *rope_sin, int rope_max_pos,
-                                                           const int32_t *seq_lens, int max_ctx, T *q, T *k,
-                                                           T *v) {
+                                                           const float *__restrict__ qkv, int splits,
+                                                           const T *__restrict__ q_norm,
+                                                           const T *__restrict__ k_norm, float eps,
+                                                           const float *__restrict__ rope_cos,
+                                                           const float *__restrict__ rope_sin, int rope_max_pos,
+                                                           const int32_t *__restrict__ seq_lens, int max_ctx,
+                                                           T *__restrict__ q, T *__restrict__ k, T *__restrict__ v) {
   const int lane = threadIdx.x & 63;
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nh = QH + 2 * KVH;
@@ -83,7 +126,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(int M, int bs, int QH
   const int i1 = own ? lane : 0, i2 = i1 + half;
   float x1 = 0.f, x2 = 0.f;
   for (int s = 0; s < splits; ++s) {
-    const float *p = part + ((size_t)s * M + m) * N + (size_t)h * D;
+    const float *p = qkv + ((size_t)s * M + m) * N + (size_t)h * D;
     x1 += p[i1];
     x2 += p[i2];
   }
@@ -129,7 +172,7 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(KvScatterArgs a) {
   const size_t col = (size_t)(l * 2 * a.KVH + kvh) * D;
   float x1 = 0.f, x2 = 0.f;
   for (int s = 0; s < a.splits; ++s) {
-    const float *p = a.part + ((size_t)s * a.N + r) * ncol + col;
+    const float *p = a.kv + ((size_t)s * a.N + r) * ncol + col;
     x1 += p[i1];
     x2 += p[i2];
   }
@@ -147,32 +190,56 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(KvScatterArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// act = round(silu(gate) * up) from the split partials [splits][M][2I] (gate then up).
 template <typename T>
-__global__ void swiglu_kernel(int M, int I, const float *part, int splits, T *act) {
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(256) void swiglu_kernel(int M, int I, const float *__restrict__ part, int splits,
+                                                     T *__restrict__ act) {
+  const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (idx >= (size_t)M * I) return;
   const int m = idx / I, n = idx % I;
-  float gsum = 0.f, usum = 0.f;
+  float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
   for (int s = 0; s < splits; ++s) {
-    const float *p = part + ((size_t)s * M + m) * (2 * (size_t)I);
-    gsum += p[n];
-    usum += p[I + n];
+    const float *p = part + ((size_t)s * M + m) * (2 * (size_t)I) + n;
+    const float4 g4 = *reinterpret_cast<const float4 *>(p);
+    const float4 u4 = *reinterpret_cast<const float4 *>(p + I);
+    gs.x += g4.x, gs.y += g4.y, gs.z += g4.z, gs.w += g4.w;
+    us.x += u4.x, us.y += u4.y, us.z += u4.z, us.w += u4.w;
   }
-  const float silu = gsum / (1.f + expf(-gsum));
-  Storage<T>::store(act, idx, silu * usum);
+  const float gv[4] = {gs.x, gs.y, gs.z, gs.w}, uv[4] = {us.x, us.y, us.z, us.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) Storage<T>::store(act, idx + c, gv[c] / (1.f + expf(-gv[c])) * uv[c]);
 }
 
 // ---------------------------------------------------------------------------------------
-// One thread per drafted row: reduce the per-64-column (max, index) pairs, lowest index on
-// ties, then assemble [bonus, drafts].
-__global__ void argmax_reduce_kernel(int B, int K, int ngroups, const float *val, const int32_t *idx,
-                                     const int32_t *bonus, int V, int32_t *draft_ids, int32_t *drafts_only) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  const int Mr = B * K;
-  if (r >= Mr) return;
+// One work-group per drafted row: reduce the per-group (max, index) pairs val/idx
+// [rows][ngroups], lowest index on ties, then assemble [bonus, drafts].
+__global__ __launch_bounds__(256) void argmax_reduce_kernel(int B, int K, int ngroups, const float *__restrict__ val,
+                                                            const int32_t *__restrict__ idx,
+                                                            const int32_t *__restrict__ bonus, int V,
+                                                            int32_t *__restrict__ draft_ids,
+                                                            int32_t *__restrict__ drafts_only) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int r = blockIdx.x;
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int gi = 0; gi < ngroups; ++gi) argmax_merge(best, bi, val[(size_t)gi * Mr + r], idx[(size_t)gi * Mr + r]);
+  const float *vr = val + (size_t)r * ngroups;
+  const int32_t *ir = idx + (size_t)r * ngroups;
+  for (int gi = threadIdx.x; gi < ngroups; gi += blockDim.x) argmax_merge(best, bi, vr[gi], ir[gi]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    argmax_merge(best, bi, ov, oi);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sv[wave] = best;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_merge(best, bi, sv[w], si[w]);
   if (bi == 0x7fffffff) bi = 0;  // every logit NaN: unspecified, but a valid id
   const int b = r / K, j = r % K;
   drafts_only[(size_t)b * K + j] = bi;
@@ -217,6 +284,7 @@ __global__ void rope_table_kernel(int D, double theta, int max_pos, float *cs, f
 hipError_t launch_embed(bool bf16, const void *embed, int V, int H, const int32_t *bonus, int B, int bs,
                         int mask_id, float *x, hipStream_t s) {
   ProfScope prof("embed", s);
+  if (H % 4) return hipErrorInvalidValue;
   if (bf16)
     embed_kernel<uint16_t><<<B * bs, 256, 0, s>>>((const uint16_t *)embed, V, H, bonus, bs, mask_id, x);
   else
@@ -224,20 +292,21 @@ hipError_t launch_embed(bool bf16, const void *embed, int V, int H, const int32_
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(bool bf16, int M, int H, float *resid, const float *part, int splits, const void *w,
+hipError_t launch_rmsnorm(bool bf16, int M, int H, float *x, const float *part, int splits, const void *w,
                           float eps, void *out, int keep_bs, void *hidden_out, hipStream_t s) {
   ProfScope prof("rmsnorm", s);
-  const size_t lds = (size_t)H * sizeof(float);
+  if (H % 4 || H > 1024 * 4 * kRmsVecs) return hipErrorInvalidValue;
+  const int threads = std::min(1024, (H / 4 + 63) / 64 * 64);
   if (bf16)
-    rmsnorm_kernel<uint16_t><<<M, 256, lds, s>>>(M, H, resid, part, splits, (const uint16_t *)w, eps,
-                                                  (uint16_t *)out, keep_bs, (uint16_t *)hidden_out);
+    rmsnorm_kernel<uint16_t><<<M, threads, 0, s>>>(M, H, x, part, splits, (const uint16_t *)w, eps, (uint16_t *)out,
+                                                keep_bs, (uint16_t *)hidden_out);
   else
-    rmsnorm_kernel<float><<<M, 256, lds, s>>>(M, H, resid, part, splits, (const float *)w, eps, (float *)out,
-                                              keep_bs, (float *)hidden_out);
+    rmsnorm_kernel<float><<<M, threads, 0, s>>>(M, H, x, part, splits, (const float *)w, eps, (float *)out, keep_bs,
+                                            (float *)hidden_out);
   return hipGetLastError();
 }
 
-hipError_t launch_qk_norm_rope(bool bf16, int M, int bs, int QH, int KVH, int D, const float *part, int splits,
+hipError_t launch_qk_norm_rope(bool bf16, int M, int bs, int QH, int KVH, int D, const float *qkv, int splits,
                                const void *q_norm, const void *k_norm, float eps, const float *rope_cos,
                                const float *rope_sin, int rope_max_pos, const int32_t *seq_lens, int max_ctx,
                                void *q, void *k, void *v, hipStream_t s) {
@@ -245,12 +314,12 @@ hipError_t launch_qk_norm_rope(bool bf16, int M, int bs, int QH, int KVH, int D,
   const int waves = M * (QH + 2 * KVH);
   const int grid = (waves + 3) / 4;
   if (bf16)
-    qk_norm_rope_kernel<uint16_t><<<grid, 256, 0, s>>>(M, bs, QH, KVH, D, part, splits, (const uint16_t *)q_norm,
+    qk_norm_rope_kernel<uint16_t><<<grid, 256, 0, s>>>(M, bs, QH, KVH, D, qkv, splits, (const uint16_t *)q_norm,
                                                        (const uint16_t *)k_norm, eps, rope_cos, rope_sin,
                                                        rope_max_pos, seq_lens, max_ctx, (uint16_t *)q,
                                                        (uint16_t *)k, (uint16_t *)v);
   else
-    qk_norm_rope_kernel<float><<<grid, 256, 0, s>>>(M, bs, QH, KVH, D, part, splits, (const float *)q_norm,
+    qk_norm_rope_kernel<float><<<grid, 256, 0, s>>>(M, bs, QH, KVH, D, qkv, splits, (const float *)q_norm,
                                                     (const float *)k_norm, eps, rope_cos, rope_sin, rope_max_pos,
                                                     seq_lens, max_ctx, (float *)q, (float *)k, (float *)v);
   return hipGetLastError();
@@ -269,7 +338,8 @@ hipError_t launch_kv_scatter(bool bf16, const KvScatterArgs &a, hipStream_t s) {
 
 hipError_t launch_swiglu(bool bf16, int M, int I, const float *part, int splits, void *act, hipStream_t s) {
   ProfScope prof("swiglu", s);
-  const size_t n = (size_t)M * I;
+  if (I % 4) return hipErrorInvalidValue;
+  const size_t n = (size_t)M * I / 4;
   const unsigned grid = (unsigned)((n + 255) / 256);
   if (bf16)
     swiglu_kernel<uint16_t><<<grid, 256, 0, s>>>(M, I, part, splits, (uint16_t *)act);
@@ -282,8 +352,7 @@ hipError_t launch_argmax_reduce(int B, int K, int ngroups, const float *val, con
                                 const int32_t *bonus, int V, int32_t *draft_ids, int32_t *drafts_only,
                                 hipStream_t s) {
   ProfScope prof("argmax_reduce", s);
-  const int n = B * K;
-  argmax_reduce_kernel<<<(n + 63) / 64, 64, 0, s>>>(B, K, ngroups, val, idx, bonus, V, draft_ids, drafts_only);
+  argmax_reduce_kernel<<<B * K, 256, 0, s>>>(B, K, ngroups, val, idx, bonus, V, draft_ids, drafts_only);
   return hipGetLastError();
 }
 

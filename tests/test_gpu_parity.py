@@ -92,3 +92,27 @@ def test_verify_matches_oracle_bit_exact():
         assert np.array_equal(acc.cpu().numpy(), ra)
         assert np.array_equal(out.cpu().numpy(), ro)
         assert np.array_equal(nb.cpu().numpy(), rn)
+
+
+def test_full_size_qwen3_b1_ctx2048_matches_oracle():
+    """The benchmark's workload at full size: Qwen3-8B-shaped bf16 drafter, batch 1, 2048-token
+    context, block size 16. Every injected cache row and every draft is compared."""
+    wl = synth.WORKLOADS["qwen3_8b_b1_ctx2048"]
+    spec = wl.spec
+    print(f"\n[case] {wl.name}", flush=True)
+    st = Setup(spec, synth.context_lengths(wl), page_size=wl.page_size, seed=wl.seed)
+    Wn = lazy_numpy(st.W)
+    kc, vc = st.oracle_cache([0], Wn)
+    _compare_cache(spec, st, kc, vc, [0])
+    bonus = synth.bonus_tokens(wl)
+    ids, drafts, hid = st.propose(bonus)
+    ref = O.propose_block(spec, Wn, kc, vc, st.bt, bonus, st.ctx, "bf16")
+    excluded = _compare_drafts(spec, ids, drafts, ref, bonus, wl.name)
+    err = check_close(spec, hid, ref["hidden"], "final hidden")
+    print(f"[case] drafts {drafts.tolist()} excluded(gap<1e-2)={excluded} hidden rel err={err:.2e}", flush=True)
+    # greedy verification of these drafts against the workload's synthetic target tokens
+    target = synth.target_tokens(wl, ref["drafts_only"])
+    acc, out, nb = binding.verify(torch.from_numpy(drafts).cuda(), torch.from_numpy(target).cuda())
+    ra, ro, rn = O.greedy_verify(drafts, target)
+    assert np.array_equal(acc.cpu().numpy(), ra) and np.array_equal(out.cpu().numpy(), ro)
+    assert np.array_equal(nb.cpu().numpy(), rn)
