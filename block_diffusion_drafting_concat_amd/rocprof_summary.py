@@ -1,0 +1,105 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+  kernel-stats:  python -m block_diffusion_drafting_concat_amd.rocprof_summary stats <run>_kernel_stats.csv
+                 prints a markdown table of per-kernel calls and durations.
+  pmc:           python -m block_diffusion_drafting_concat_amd.rocprof_summary pmc <workload> \
+                     <fetch>_counter_collection.csv <write>_counter_collection.csv
+                 prints the JSON read by bench.py: per GEMM instance, the HBM bytes per launch
+                 from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the same
+                 counter reads for the largest plain device copy in the run (bench.py
+                 --copy-calib copies 1 GiB), so that bytes = counter * (copy bytes / copy reading).
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GEMM_SOURCES = ("block_diffusion_drafting_concat_amd/csrc/gemm.hip", "block_diffusion_drafting_concat_amd/csrc/common.h")
+EPI = {"0": "kStore", "1": "kResidAdd", "2": "kSwiGLU", "3": "kArgmax"}
+COPY_BYTES = 1 << 30
+
+
+def source_sha(paths=GEMM_SOURCES) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    """'gemm_kernel<unsigned short, 1, 8, 1, (dflash::GemmEpi)3, false>(...)' ->
+    'gemm_kernel<bf16,MT=1,CW=8,KW=1,kArgmax>'; other kernels: the name without arguments."""
+    m = re.search(r"gemm_kernel<([^,]+), (\d+), (\d+), (\d+), \(dflash::GemmEpi\)(\d), (true|false)>", name)
+    if m:
+        dt = "bf16" if "short" in m.group(1) else "f32"
+        s = f"gemm_kernel<{dt},MT={m.group(2)},CW={m.group(3)},KW={m.group(4)},{EPI[m.group(5)]}"
+        return s + (",multi-A>" if m.group(6) == "true" else ">")
+    name = re.sub(r"^void ", "", name)
+    name = name.replace("dflash::(anonymous namespace)::", "")
+    return re.sub(r"\(.*$", "", name)
+
+
+def stats(path: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["| kernel | calls | avg us | total ms | % |", "|---|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
+    return "\n".join(out)
+
+
+def _counter(path: str, counter: str):
+    per = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def pmc(workload: str, fetch_csv: str, write_csv: str) -> dict:
+    f = _counter(fetch_csv, "FETCH_SIZE")
+    w = _counter(write_csv, "WRITE_SIZE")
+    copies_f = [v for k, vs in f.items() if "copyBuffer" in k for v in vs]
+    copies_w = [v for k, vs in w.items() if "copyBuffer" in k for v in vs]
+    if not copies_f or not copies_w:
+        raise SystemExit("no device copy found: run bench.py with --copy-calib")
+    kib = COPY_BYTES / 1024
+    scale_f = kib / max(copies_f)
+    scale_w = kib / max(copies_w)
+    kernels = {}
+    for k in set(f) | set(w):
+        s = short_name(k)
+        if not s.startswith("gemm_kernel") and not s.startswith("attn_"):
+            continue
+        fk = sum(f.get(k, [0])) / max(1, len(f.get(k, [])))
+        wk = sum(w.get(k, [0])) / max(1, len(w.get(k, [])))
+        kernels[s] = {"fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
+                      "traffic_bytes_per_launch": (fk * scale_f + wk * scale_w) * 1024,
+                      "launches": len(f.get(k, []))}
+    return {"workload": workload, "source_sha": source_sha(), "copy_bytes": COPY_BYTES,
+            "copy_fetch_kib": max(copies_f), "copy_write_kib": max(copies_w),
+            "scale_fetch": scale_f, "scale_write": scale_w, "kernels": kernels}
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[0] == "stats":
+        print(stats(argv[1]))
+    elif len(argv) >= 4 and argv[0] == "pmc":
+        print(json.dumps(pmc(argv[1], argv[2], argv[3]), indent=1))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
