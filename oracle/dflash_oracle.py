@@ -14,10 +14,16 @@ three web pages:
 The pages fix neither the precision nor several details of the layer. Where they are silent
 the docstrings below say "reading" and state the reading taken.
 
-Storage rounding.  The GPU path stores GEMM operands and KV entries in the drafter's storage
-type (bf16 or fp32) and keeps everything else in fp32. The oracle computes in fp64 and rounds
-to the storage type at exactly those points (`rho`). mode="exact" turns the rounding off
-(a precision diagnostic, and what the transformers-based pins compare against).
+Storage rounding (reading: the pages fix no precision).  Weights and the KV cache are held in
+the drafter's storage type (bf16 or fp32); the block's own q, k and v, which enter attention
+alongside cached keys and values, are rounded to it as well. Every other activation, including
+every GEMM input, the residual stream, norms, softmax and logits, is kept exact: in fp32 on the
+GPU, where a bf16 GEMM takes an fp32 activation as an exact pair of bf16 halves. Rounding every
+GEMM input instead would make two correct implementations drift apart by about one bf16 unit
+per element after a few layers, since each rounding disagreement is spread by the next dense
+product into the following rounding point. The oracle computes in fp64 and rounds at exactly
+the points above (`rho`). mode="exact" turns all rounding off (a precision diagnostic, and what
+the transformers-based pins compare against).
 
 Array conventions: dense weights are row-major [out, in] (y = W x, the F.linear convention).
 Each KV cache is a list over layers of float32 arrays [num_pages, page_size, n_kv_heads,
@@ -151,14 +157,14 @@ def inject_context_kv(spec, W, k_cache, v_cache, aux, positions, slot_mapping, m
     the fused K/V projection to ctx directly). Fusing the layers' K/V weights into one matrix
     is a re-association of the same product, so per-layer projections are used here.
 
-    Returns {"y": fc output, "ctx": rounded hidden_norm output} for the kept rows."""
+    Returns {"y": fc output, "ctx": hidden_norm output} for the kept rows."""
     rho = storage_rounding(mode)
     slot = np.asarray(slot_mapping, dtype=np.int64)
     keep = np.nonzero(slot >= 0)[0]
     pos = np.asarray(positions, dtype=np.int64)[keep]
     x = np.concatenate([f64(a)[keep] for a in aux], axis=1)
     y = x @ f64(W["fc"]).T
-    ctx = rho(rms_norm(y, W["hidden_norm"], spec.rms_eps))
+    ctx = rms_norm(y, W["hidden_norm"], spec.rms_eps)  # a GEMM input: kept exact
     P = k_cache[0].shape[1]
     page, off = slot[keep] // P, slot[keep] % P
     KVH, D = spec.n_kv_heads, spec.head_dim
@@ -221,7 +227,7 @@ def propose_block(spec, W, k_cache, v_cache, block_table, bonus, seq_lens, mode:
     the drafts.
 
     Returns dict(draft_token_ids [B, bs], drafts_only [B, K], hidden [B*K, H] (final-norm
-    output, rounded), gap [B, K] top-2 logit gap, and optionally logits)."""
+    output), gap [B, K] top-2 logit gap, and optionally logits)."""
     rho = storage_rounding(mode)
     H, QH, KVH, D = spec.hidden, spec.n_q_heads, spec.n_kv_heads, spec.head_dim
     G = QH // KVH
@@ -235,7 +241,7 @@ def propose_block(spec, W, k_cache, v_cache, block_table, bonus, seq_lens, mode:
     x = f64(np.asarray(W["embed"])[ids])  # residual stream [B*bs, H], never rounded
     for l in range(spec.n_layers):
         p = f"layers.{l}."
-        h = rho(rms_norm(x, W[p + "in_norm"], eps))
+        h = rms_norm(x, W[p + "in_norm"], eps)
         q = (h @ f64(W[p + "wq"]).T).reshape(-1, QH, D)
         k = (h @ f64(W[p + "wk"]).T).reshape(-1, KVH, D)
         v = (h @ f64(W[p + "wv"]).T).reshape(-1, KVH, D)
@@ -254,13 +260,13 @@ def propose_block(spec, W, k_cache, v_cache, block_table, bonus, seq_lens, mode:
             for hq in range(QH):
                 g = hq // G  # reading: q head h uses kv head h // G
                 o[rows, hq] = attention(q[rows, hq], keys[:, g], vals[:, g])
-        x = x + rho(o).reshape(B * bs, QH * D) @ f64(W[p + "wo"]).T
-        h2 = rho(rms_norm(x, W[p + "post_norm"], eps))
+        x = x + o.reshape(B * bs, QH * D) @ f64(W[p + "wo"]).T
+        h2 = rms_norm(x, W[p + "post_norm"], eps)
         gate = h2 @ f64(W[p + "w_gate"]).T
         up = h2 @ f64(W[p + "w_up"]).T
-        x = x + rho(silu(gate) * up) @ f64(W[p + "w_down"]).T
+        x = x + (silu(gate) * up) @ f64(W[p + "w_down"]).T
 
-    f = rho(rms_norm(x[keep], W["final_norm"], eps))
+    f = rms_norm(x[keep], W["final_norm"], eps)
     tok, gap, z = _lm_head_argmax(f, W["lm_head"])
     drafts = tok.reshape(B, K).astype(np.int32)
     out = {"draft_token_ids": np.concatenate([bonus[:, None].astype(np.int32), drafts], axis=1),
