@@ -104,7 +104,7 @@ InjectPlan plan_inject(const dflash_config *c, int rows) {
   const size_t part = std::max((size_t)p.s_fc * c->hidden, (size_t)p.s_kv * kvn) * rows * sizeof(float);
   Carver cv;
   p.off_part = cv.take(part);
-  p.off_ctx = cv.take((size_t)rows * c->hidden * elem_size(c));
+  p.off_ctx = cv.take((size_t)rows * c->hidden * sizeof(float));
   p.total = cv.off;
   return p;
 }
@@ -139,14 +139,14 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
                       p.M * sizeof(float);
   Carver cv;
   p.off_x = cv.take((size_t)p.M * H * sizeof(float));
-  p.off_h = cv.take((size_t)p.M * H * es);
+  p.off_h = cv.take((size_t)p.M * H * sizeof(float));
   p.off_part = cv.take(part);
   p.off_q = cv.take((size_t)p.M * QH * D * es);
   p.off_k = cv.take((size_t)p.M * KVH * D * es);
   p.off_v = cv.take((size_t)p.M * KVH * D * es);
-  p.off_o = cv.take((size_t)p.M * QH * D * es);
-  p.off_act = cv.take((size_t)p.M * I * es);
-  p.off_f = cv.take((size_t)std::max(p.Mk, 1) * H * es);
+  p.off_o = cv.take((size_t)p.M * QH * D * sizeof(float));
+  p.off_act = cv.take((size_t)p.M * I * sizeof(float));
+  p.off_f = cv.take((size_t)std::max(p.Mk, 1) * H * sizeof(float));
   const size_t nrow = (size_t)B * KVH * p.nsplit * 64;
   p.off_po = cv.take(nrow * D * sizeof(float));
   p.off_pm = cv.take(nrow * sizeof(float));
@@ -192,6 +192,7 @@ GemmArgs gemm_args(const char *tag, const void *a, int64_t lda, int M, int N, in
   g.N = N;
   g.K = K;
   g.tag = tag;
+  g.a_f32 = true;  // activations are fp32; only the auxiliary states are bf16
   return g;
 }
 
@@ -290,13 +291,14 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
       return fail(DFLASH_ERR_WORKSPACE_TOO_SMALL, "inject needs %zu workspace bytes, got %zu", p.total,
                   workspace_bytes);
     float *part = at<float>(workspace, p.off_part);
-    void *ctx = at<char>(workspace, p.off_ctx);
+    float *ctx = at<float>(workspace, p.off_ctx);
 
     // fc over the concatenated auxiliary states, read in place from the n_aux pointers
     GemmArgs g = gemm_args("gemm.fc", nullptr, aux_row_stride, rows, H, cfg->n_aux * cfg->target_hidden);
     for (int j = 0; j < cfg->n_aux; ++j)
       g.a[j] = static_cast<const char *>(aux[j]) + (size_t)r0 * aux_row_stride * es;
     g.a_nseg = cfg->n_aux;
+    g.a_f32 = false;  // the auxiliary states come in the storage type
     g.b[0] = w->fc;
     g.b_end[0] = H;
     g.out = part;
@@ -339,7 +341,7 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
 dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weights *w, const dflash_kv_cache *cache,
                                    int32_t batch, const int32_t *bonus_tokens, const int32_t *seq_lens,
                                    int32_t max_context, int32_t *draft_token_ids, int32_t *drafts_only,
-                                   void *hidden_out, void *workspace, size_t workspace_bytes, void *stream) {
+                                   float *hidden_out, void *workspace, size_t workspace_bytes, void *stream) {
   dflash_status st = check_config(cfg);
   if (st != DFLASH_OK) return st;
   if (batch < 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "batch < 0");
@@ -372,14 +374,14 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
   const int H = cfg->hidden, D = cfg->head_dim, QH = cfg->n_q_heads, KVH = cfg->n_kv_heads;
   const int I = cfg->intermediate, bs = cfg->block_size, K = bs - 1, M = p.M;
   float *x = at<float>(workspace, p.off_x);
-  void *h = at<char>(workspace, p.off_h);
+  float *h = at<float>(workspace, p.off_h);
   float *part = at<float>(workspace, p.off_part);
   void *q = at<char>(workspace, p.off_q);
   void *kb = at<char>(workspace, p.off_k);
   void *vb = at<char>(workspace, p.off_v);
-  void *o = at<char>(workspace, p.off_o);
-  void *act = at<char>(workspace, p.off_act);
-  void *f = at<char>(workspace, p.off_f);
+  float *o = at<float>(workspace, p.off_o);
+  float *act = at<float>(workspace, p.off_act);
+  float *f = at<float>(workspace, p.off_f);
 
   HIP_TRY(launch_embed(bf, w->embed, cfg->vocab, H, bonus_tokens, batch, bs, cfg->mask_token_id, x, s));
   int pending = 0;  // split count of down-projection partials not yet added to x

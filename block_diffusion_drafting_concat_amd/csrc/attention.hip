@@ -225,7 +225,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
   }
   const float den = block_sum(dloc, red);  // synchronises, so wsplit is visible
   const int hh = row / a.bs, j = row % a.bs;
-  T *o = reinterpret_cast<T *>(a.o) + ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D;
+  float *o = a.o + ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     const float *po = a.po + (base + row) * D + d;
     float num = 0.f;
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
       num += wsplit[s + 3] * p3;
     }
     for (; s < ns; ++s) num += wsplit[s] * po[(size_t)s * 64 * D];
-    Storage<T>::store(o, d, num / den);
+    o[d] = num / den;
   }
 }
 

@@ -12,7 +12,7 @@
 //  * the activation slice is staged in LDS (in passes of at most kPassBytes), so A fragments
 //    come from LDS and the vector-memory path carries only weights;
 //  * the KW sub-slice tiles are summed through LDS in a fixed order. With one split the
-//    epilogue is applied in place (fp32 store, residual add, SwiGLU, or the LM head's
+//    epilogue is applied in place (fp32 store, residual add, fp32 SwiGLU, or the LM head's
 //    (max, lowest index) per work-group); with several, fp32 partials [split][M][N] go to
 //    the workspace and the consumer kernel sums them in split order. There are no float
 //    atomics, so results are deterministic.
@@ -31,7 +31,10 @@ __host__ __device__ constexpr int ch_of() {
   return 4 * Storage<T>::kPerVec;  // K elements per wave MFMA step
 }
 
-template <typename T, int MT, int CW, int KW, GemmEpi E, bool kMultiA>
+// kAF32: the activation A is fp32 while W is bf16. A is staged in LDS as two bf16 planes,
+// hi = bf16(a) and lo = bf16(a - hi), and every K step issues two MFMAs (hi*W + lo*W), so
+// the product sees A to ~16 significant bits instead of bf16's 8.
+template <typename T, int MT, int CW, int KW, GemmEpi E, bool kMultiA, bool kAF32>
 __global__ __launch_bounds__(CW *KW * 64) void gemm_kernel(GemmArgs g) {
   constexpr int NW = CW * KW;
   constexpr int KPV = Storage<T>::kPerVec;
@@ -39,6 +42,8 @@ __global__ __launch_bounds__(CW *KW * 64) void gemm_kernel(GemmArgs g) {
   constexpr bool kDual = E == GemmEpi::kSwiGLU;
   constexpr int NACC = kDual ? 2 : 1;
   constexpr int U = kGroup;
+  constexpr int NPL = kAF32 ? 2 : 1;  // A planes in LDS
+  static_assert(!kAF32 || (KPV == 8 && !kMultiA), "fp32 activations pair with bf16 weights");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T *sa = reinterpret_cast<T *>(smem);
   float *red = reinterpret_cast<float *>(smem);
@@ -76,8 +81,9 @@ __global__ __launch_bounds__(CW *KW * 64) void gemm_kernel(GemmArgs g) {
   // The loads below are issued unconditionally (addresses clamped into the operand) so that
   // the compiler can count outstanding loads exactly: weight loads stay in flight across the
   // A staging and across each MFMA group (register double buffering).
-  const int vrow = kp / KPV;  // 16-byte vectors per staged A row
-  constexpr int NA = (kPassBytes / 16 + NW * 64 - 1) / (NW * 64);  // A vectors per thread, max
+  const int vrow = kp / KPV;  // 16-byte vectors per staged A row (per plane)
+  constexpr int NA = (kPassBytes / (16 * NPL) + NW * 64 - 1) / (NW * 64);  // A vectors per thread, max
+  T *sa_lo = sa + 16 * MT * as;  // lo plane (kAF32)
   for (int p0 = kb; p0 < ke; p0 += kp) {
     const int plen = min(kp, ke - p0);  // a multiple of CH
     const int q0 = kw * kq;
@@ -98,30 +104,42 @@ __global__ __launch_bounds__(CW *KW * 64) void gemm_kernel(GemmArgs g) {
         const int k = q0 + (st0 + u) * CH;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
+          const int ao = (t * 16 + (lane & 15)) * as + k + kg;
           Vec16 af;
-          af.u = *reinterpret_cast<const uint4 *>(sa + (t * 16 + (lane & 15)) * as + k + kg);
+          af.u = *reinterpret_cast<const uint4 *>(sa + ao);
 #pragma unroll
           for (int a = 0; a < NACC; ++a) mma16<T>(acc[a][t], af, b[a][u]);
+          if constexpr (kAF32) {
+            af.u = *reinterpret_cast<const uint4 *>(sa_lo + ao);
+#pragma unroll
+            for (int a = 0; a < NACC; ++a) mma16<T>(acc[a][t], af, b[a][u]);
+          }
         }
       }
     };
 
     // ---- A rows [m0, m0 + 16*MT) x K [p0, p0 + plen): loads first, then weights group 0
-    Vec16 areg[NA];
+    Vec16 areg[NA][NPL];
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       const int v = min((int)threadIdx.x + j * NW * 64, total - 1);
       const int r = v / vrow, cv = v % vrow;
       const int m = min(m0 + r, g.M - 1);
       const int k = p0 + min(cv * KPV, plen - KPV);
-      const T *ap;
-      if (kMultiA) {
-        const int s = k / a_seglen;
-        ap = reinterpret_cast<const T *>(g.a[s]) + (k - s * a_seglen);
+      if constexpr (kAF32) {  // 8 fp32 values = two 16-byte loads
+        const float *ap = reinterpret_cast<const float *>(g.a[0]) + (size_t)m * g.lda + k;
+        areg[j][0] = load_vec16(ap);
+        areg[j][NPL - 1] = load_vec16(ap + 4);
       } else {
-        ap = reinterpret_cast<const T *>(g.a[0]) + k;
+        const T *ap;
+        if (kMultiA) {
+          const int s = k / a_seglen;
+          ap = reinterpret_cast<const T *>(g.a[s]) + (k - s * a_seglen);
+        } else {
+          ap = reinterpret_cast<const T *>(g.a[0]) + k;
+        }
+        areg[j][0] = load_vec16(ap + (size_t)m * g.lda);
       }
-      areg[j] = load_vec16(ap + (size_t)m * g.lda);
     }
     Vec16 b0[NACC][U], b1[NACC][U];
     load_group(b0, 0);
@@ -132,7 +150,22 @@ __global__ __launch_bounds__(CW *KW * 64) void gemm_kernel(GemmArgs g) {
       if (v < total) {
         const int r = v / vrow, cv = v % vrow;
         const bool ok = m0 + r < g.M && cv * KPV < plen;
-        *reinterpret_cast<uint4 *>(sa + r * as + cv * KPV) = ok ? areg[j].u : make_uint4(0, 0, 0, 0);
+        if constexpr (kAF32) {
+          float f[8];
+          __builtin_memcpy(f, &areg[j][0].u, 16);
+          __builtin_memcpy(f + 4, &areg[j][NPL - 1].u, 16);
+          uint16_t hi[8], lo[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = ok ? f[e] : 0.f;
+            hi[e] = f32_to_bf16(x);
+            lo[e] = f32_to_bf16(x - bf16_to_f32(hi[e]));
+          }
+          __builtin_memcpy(sa + r * as + cv * KPV, hi, 16);
+          __builtin_memcpy(sa_lo + r * as + cv * KPV, lo, 16);
+        } else {
+          *reinterpret_cast<uint4 *>(sa + r * as + cv * KPV) = ok ? areg[j][0].u : make_uint4(0, 0, 0, 0);
+        }
       }
     }
     __syncthreads();
@@ -160,10 +193,16 @@ __global__ __launch_bounds__(CW *KW * 64) void gemm_kernel(GemmArgs g) {
       for (int a = 0; a < NACC; ++a) bf[a] = load_vec16(brow[a] + p0 + k);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
+        const int ao = (t * 16 + (lane & 15)) * as + k + kg;
         Vec16 af;
-        af.u = *reinterpret_cast<const uint4 *>(sa + (t * 16 + (lane & 15)) * as + k + kg);
+        af.u = *reinterpret_cast<const uint4 *>(sa + ao);
 #pragma unroll
         for (int a = 0; a < NACC; ++a) mma16<T>(acc[a][t], af, bf[a]);
+        if constexpr (kAF32) {
+          af.u = *reinterpret_cast<const uint4 *>(sa_lo + ao);
+#pragma unroll
+          for (int a = 0; a < NACC; ++a) mma16<T>(acc[a][t], af, bf[a]);
+        }
       }
     }
   }
@@ -211,7 +250,7 @@ __global__ __launch_bounds__(CW *KW * 64) void gemm_kernel(GemmArgs g) {
         g.out[o] += v[0];
       } else if constexpr (E == GemmEpi::kSwiGLU) {
         const float silu = v[0] / (1.f + expf(-v[0]));
-        Storage<T>::store(reinterpret_cast<T *>(g.act), o, silu * v[NACC - 1]);
+        g.act[o] = silu * v[NACC - 1];
       }
     }
   }
@@ -254,44 +293,47 @@ Shape pick_shape(int M, GemmEpi epi) {
   return {4, 2};
 }
 
-template <typename T, int MT, int CW, int KW, GemmEpi E>
+template <typename T, int MT, int CW, int KW, GemmEpi E, bool kAF32>
 size_t lds_bytes(const GemmArgs &g) {
   constexpr int KPV = Storage<T>::kPerVec;
-  const size_t a = (size_t)16 * MT * (g.kp + KPV) * sizeof(T);
+  const size_t a = (size_t)16 * MT * (g.kp + KPV) * sizeof(T) * (kAF32 ? 2 : 1);
   const int nacc = E == GemmEpi::kSwiGLU ? 2 : 1;
   size_t r = (size_t)CW * KW * nacc * 256 * sizeof(float);
   if (E == GemmEpi::kArgmax) r += (size_t)CW * MT * 256 * sizeof(float);
   return a > r ? a : r;
 }
 
-template <typename T, int MT, int CW, int KW, GemmEpi E, bool kMultiA>
+template <typename T, int MT, int CW, int KW, GemmEpi E, bool kMultiA, bool kAF32>
 hipError_t launch_k(const GemmArgs &g, int splits, hipStream_t s) {
   dim3 grid((g.N + 16 * CW - 1) / (16 * CW), splits, (g.M + 16 * MT - 1) / (16 * MT));
-  gemm_kernel<T, MT, CW, KW, E, kMultiA><<<grid, CW * KW * 64, lds_bytes<T, MT, CW, KW, E>(g), s>>>(g);
+  gemm_kernel<T, MT, CW, KW, E, kMultiA, kAF32>
+      <<<grid, CW * KW * 64, lds_bytes<T, MT, CW, KW, E, kAF32>(g), s>>>(g);
   return hipGetLastError();
 }
 
-template <typename T, GemmEpi E, bool kMultiA>
+template <typename T, GemmEpi E, bool kMultiA, bool kAF32>
 hipError_t launch_t(const GemmArgs &g, int splits, hipStream_t s) {
   switch (gemm_mt(g.M)) {
     case 1:
-      if constexpr (E == GemmEpi::kArgmax) return launch_k<T, 1, 8, 1, E, kMultiA>(g, splits, s);
-      else return launch_k<T, 1, 4, 2, E, kMultiA>(g, splits, s);
-    case 2: return launch_k<T, 2, 2, 2, E, kMultiA>(g, splits, s);
-    case 3: return launch_k<T, 3, 2, 2, E, kMultiA>(g, splits, s);
-    default: return launch_k<T, 4, 2, 2, E, kMultiA>(g, splits, s);
+      if constexpr (E == GemmEpi::kArgmax) return launch_k<T, 1, 8, 1, E, kMultiA, kAF32>(g, splits, s);
+      else return launch_k<T, 1, 4, 2, E, kMultiA, kAF32>(g, splits, s);
+    case 2: return launch_k<T, 2, 2, 2, E, kMultiA, kAF32>(g, splits, s);
+    case 3: return launch_k<T, 3, 2, 2, E, kMultiA, kAF32>(g, splits, s);
+    default: return launch_k<T, 4, 2, 2, E, kMultiA, kAF32>(g, splits, s);
   }
 }
 
-template <typename T>
+// fp32 drafters: A and W are fp32. bf16 drafters: W is bf16 and A is either bf16 (the
+// auxiliary states of injection, possibly in several segments) or fp32 (every activation).
+template <typename T, bool kAF32>
 hipError_t launch_dt(const GemmArgs &g, GemmEpi epi, int splits, hipStream_t s) {
-  const bool multi = g.a_nseg > 1;
   switch (epi) {
     case GemmEpi::kStore:
-      return multi ? launch_t<T, GemmEpi::kStore, true>(g, splits, s) : launch_t<T, GemmEpi::kStore, false>(g, splits, s);
-    case GemmEpi::kResidAdd: return launch_t<T, GemmEpi::kResidAdd, false>(g, splits, s);
-    case GemmEpi::kSwiGLU: return launch_t<T, GemmEpi::kSwiGLU, false>(g, splits, s);
-    default: return launch_t<T, GemmEpi::kArgmax, false>(g, splits, s);
+      if (g.a_nseg > 1) return launch_t<T, GemmEpi::kStore, true, false>(g, splits, s);
+      return launch_t<T, GemmEpi::kStore, false, kAF32>(g, splits, s);
+    case GemmEpi::kResidAdd: return launch_t<T, GemmEpi::kResidAdd, false, kAF32>(g, splits, s);
+    case GemmEpi::kSwiGLU: return launch_t<T, GemmEpi::kSwiGLU, false, kAF32>(g, splits, s);
+    default: return launch_t<T, GemmEpi::kArgmax, false, kAF32>(g, splits, s);
   }
 }
 
@@ -329,11 +371,13 @@ hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, int splits, h
   g.kt = g.K / splits;
   // K per staged pass: the split cut into equal passes that fit the LDS budget
   const int mt = gemm_mt(g.M);
-  const int esz = bf16 ? 2 : 4;
+  const bool af32 = bf16 && g.a_f32 && g.a_nseg == 1;
+  const int esz = (bf16 && !af32) ? 2 : 4;  // LDS bytes per staged A element
   const int kp_max = kPassBytes / (16 * mt * esz) / step * step;
   const int npass = (g.kt + kp_max - 1) / kp_max;
   g.kp = ((g.kt + npass - 1) / npass + step - 1) / step * step;
-  return bf16 ? launch_dt<uint16_t>(g, epi, splits, s) : launch_dt<float>(g, epi, splits, s);
+  if (!bf16) return launch_dt<float, false>(g, epi, splits, s);
+  return af32 ? launch_dt<uint16_t, true>(g, epi, splits, s) : launch_dt<uint16_t, false>(g, epi, splits, s);
 }
 
 }  // namespace dflash

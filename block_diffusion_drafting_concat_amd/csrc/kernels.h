@@ -15,7 +15,7 @@ namespace dflash {
 // With one K split the epilogue is applied in the same kernel:
 //   kStore    out[m][n] = C                                   (fp32)
 //   kResidAdd out[m][n] += C                                  (the fp32 residual stream)
-//   kSwiGLU   act[m][n] = round(silu(C_gate) * C_up), B = {gate [N,K], up [N,K]}
+//   kSwiGLU   act[m][n] = silu(C_gate) * C_up (fp32), B = {gate [N,K], up [N,K]}
 //   kArgmax   amax_{val,idx}[m][g] = (max, lowest index) over column group g (one split only)
 // With `splits` > 1 every split writes fp32 partials part[s][m][N] (SwiGLU: part[s][m][2N],
 // gate then up) and the consumer kernel sums them in split order.
@@ -34,10 +34,11 @@ struct GemmArgs {
   int b_nseg;
   int M, N, K;
   float *out;         // kStore / kResidAdd: [M][N]
-  void *act;          // kSwiGLU: [M][N] of the storage type
+  float *act;         // kSwiGLU: [M][N] fp32
   float *part;        // splits > 1: [splits][M][N] (SwiGLU [splits][M][2N])
   float *amax_val;    // kArgmax: [M][gemm_col_groups(N)]
   int32_t *amax_idx;  // kArgmax: [M][gemm_col_groups(N)]
+  bool a_f32;         // A is fp32 (single segment) while B is bf16: hi+lo bf16 MFMA pairs
   const char *tag;    // name under which the launch is timed when profiling is on
   int kt, kp;         // set by launch_gemm: K per split, K per staged LDS pass
 };
@@ -56,12 +57,12 @@ hipError_t launch_embed(bool bf16, const void *embed, int V, int H, const int32_
                         int B, int bs, int mask_id, float *x, hipStream_t s);
 
 // For each row m: r = (x ? x[m] : 0) + sum_s part[s][m] (split order); if x and splits,
-// x[m] = r; out[row_map(m)] = round(rmsnorm(r) * w). With keep_bs > 0 only rows with
+// x[m] = r; out[row_map(m)] = rmsnorm(r) * w (fp32). With keep_bs > 0 only rows with
 // m % keep_bs != 0 are normalised, and they are written compactly (block slot 0 dropped):
 // out row (m / keep_bs) * (keep_bs - 1) + m % keep_bs - 1. hidden_out (optional) gets the
 // same rows.
 hipError_t launch_rmsnorm(bool bf16, int M, int H, float *x, const float *part, int splits,
-                          const void *w, float eps, void *out, int keep_bs, void *hidden_out,
+                          const void *w, float eps, float *out, int keep_bs, float *hidden_out,
                           hipStream_t s);
 
 // q/k/v of the block from the fp32 QKV projection partials [splits][M][(QH+2KVH)*D]: per-head
@@ -92,8 +93,8 @@ struct KvScatterArgs {
 };
 hipError_t launch_kv_scatter(bool bf16, const KvScatterArgs &a, hipStream_t s);
 
-// act[m][n] = round(silu(sum_s part[s][m][n]) * sum_s part[s][m][I + n]), part [splits][M][2I].
-hipError_t launch_swiglu(bool bf16, int M, int I, const float *part, int splits, void *act,
+// act[m][n] = silu(sum_s part[s][m][n]) * sum_s part[s][m][I + n] (fp32), part [splits][M][2I].
+hipError_t launch_swiglu(bool bf16, int M, int I, const float *part, int splits, float *act,
                          hipStream_t s);
 
 // Final argmax over the column groups val/idx [B*K][ngroups] (lowest index on ties) and
@@ -121,7 +122,7 @@ struct AttnArgs {
   int B, bs, QH, KVH, D;
   int chunk, nsplit;  // keys per split (multiple of 64), splits per sequence
   float *po, *pm, *pl;  // partials [B][KVH][nsplit][64][D], [B][KVH][nsplit][64]
-  void *o;              // merged output [M][QH*D]
+  float *o;             // merged output [M][QH*D], fp32
 };
 void attn_plan(int B, int KVH, int max_keys, int *chunk, int *nsplit);
 hipError_t launch_attention(bool bf16, const AttnArgs &a, hipStream_t s);

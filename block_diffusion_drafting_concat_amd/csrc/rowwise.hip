@@ -38,15 +38,15 @@ __global__ __launch_bounds__(256) void embed_kernel(const T *__restrict__ embed,
 }
 
 // ---------------------------------------------------------------------------------------
-// r = (x[m] or 0) + sum_s part[s][m]; x[m] = r; out = round(r / rms(r) * w). One work-group
+// r = (x[m] or 0) + sum_s part[s][m]; x[m] = r; out = r / rms(r) * w (fp32). One work-group
 // of up to 1024 threads per row; each thread owns at most kRmsVecs float4 of the row and
 // the split loop is unrolled so that the partials stream in parallel.
 constexpr int kRmsVecs = 4;
 template <typename T>
 __global__ __launch_bounds__(1024) void rmsnorm_kernel(int M, int H, float *__restrict__ x,
                                                       const float *__restrict__ part, int splits,
-                                                      const T *__restrict__ w, float eps, T *__restrict__ out,
-                                                      int keep_bs, T *__restrict__ hidden_out) {
+                                                      const T *__restrict__ w, float eps, float *__restrict__ out,
+                                                      int keep_bs, float *__restrict__ hidden_out) {
   __shared__ float red[16];
   const int m = blockIdx.x;
   if (keep_bs > 0 && m % keep_bs == 0) return;  // block slot 0 is not drafted
@@ -88,8 +88,8 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(int M, int H, float *__re
     for (int c = 0; c < 4; ++c) {
       const size_t col = (size_t)i * 4 + c;
       const float y = e[c] * inv * Storage<T>::load(w, col);
-      Storage<T>::store(out, (size_t)orow * H + col, y);
-      if (hidden_out) Storage<T>::store(hidden_out, (size_t)orow * H + col, y);
+      out[(size_t)orow * H + col] = y;
+      if (hidden_out) hidden_out[(size_t)orow * H + col] = y;
     }
   }
 }
@@ -190,10 +190,10 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(KvScatterArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// act = round(silu(gate) * up) from the split partials [splits][M][2I] (gate then up).
+// act = silu(gate) * up (fp32) from the split partials [splits][M][2I] (gate then up).
 template <typename T>
 __global__ __launch_bounds__(256) void swiglu_kernel(int M, int I, const float *__restrict__ part, int splits,
-                                                     T *__restrict__ act) {
+                                                     float *__restrict__ act) {
   const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (idx >= (size_t)M * I) return;
   const int m = idx / I, n = idx % I;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(int M, int I, const float *
   }
   const float gv[4] = {gs.x, gs.y, gs.z, gs.w}, uv[4] = {us.x, us.y, us.z, us.w};
 #pragma unroll
-  for (int c = 0; c < 4; ++c) Storage<T>::store(act, idx + c, gv[c] / (1.f + expf(-gv[c])) * uv[c]);
+  for (int c = 0; c < 4; ++c) act[idx + c] = gv[c] / (1.f + expf(-gv[c])) * uv[c];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -293,16 +293,16 @@ hipError_t launch_embed(bool bf16, const void *embed, int V, int H, const int32_
 }
 
 hipError_t launch_rmsnorm(bool bf16, int M, int H, float *x, const float *part, int splits, const void *w,
-                          float eps, void *out, int keep_bs, void *hidden_out, hipStream_t s) {
+                          float eps, float *out, int keep_bs, float *hidden_out, hipStream_t s) {
   ProfScope prof("rmsnorm", s);
   if (H % 4 || H > 1024 * 4 * kRmsVecs) return hipErrorInvalidValue;
   const int threads = std::min(1024, (H / 4 + 63) / 64 * 64);
   if (bf16)
-    rmsnorm_kernel<uint16_t><<<M, threads, 0, s>>>(M, H, x, part, splits, (const uint16_t *)w, eps, (uint16_t *)out,
-                                                keep_bs, (uint16_t *)hidden_out);
+    rmsnorm_kernel<uint16_t><<<M, threads, 0, s>>>(M, H, x, part, splits, (const uint16_t *)w, eps, out, keep_bs,
+                                                hidden_out);
   else
-    rmsnorm_kernel<float><<<M, threads, 0, s>>>(M, H, x, part, splits, (const float *)w, eps, (float *)out, keep_bs,
-                                            (float *)hidden_out);
+    rmsnorm_kernel<float><<<M, threads, 0, s>>>(M, H, x, part, splits, (const float *)w, eps, out, keep_bs,
+                                            hidden_out);
   return hipGetLastError();
 }
 
@@ -336,15 +336,15 @@ hipError_t launch_kv_scatter(bool bf16, const KvScatterArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu(bool bf16, int M, int I, const float *part, int splits, void *act, hipStream_t s) {
+hipError_t launch_swiglu(bool bf16, int M, int I, const float *part, int splits, float *act, hipStream_t s) {
   ProfScope prof("swiglu", s);
   if (I % 4) return hipErrorInvalidValue;
   const size_t n = (size_t)M * I / 4;
   const unsigned grid = (unsigned)((n + 255) / 256);
   if (bf16)
-    swiglu_kernel<uint16_t><<<grid, 256, 0, s>>>(M, I, part, splits, (uint16_t *)act);
+    swiglu_kernel<uint16_t><<<grid, 256, 0, s>>>(M, I, part, splits, act);
   else
-    swiglu_kernel<float><<<grid, 256, 0, s>>>(M, I, part, splits, (float *)act);
+    swiglu_kernel<float><<<grid, 256, 0, s>>>(M, I, part, splits, act);
   return hipGetLastError();
 }
 

@@ -17,9 +17,10 @@
  *    synchronisation. Ordering between calls (e.g. inject before propose on the same cache)
  *    follows stream order and is the caller's job. Calls sharing a workspace must not overlap.
  *  - Dense weights are row-major [out_features, in_features] (y = W x). Weights, auxiliary
- *    states, activations and KV caches use the config's storage dtype: bfloat16 (raw 16-bit
- *    bf16 values) or fp32. The RoPE table is always fp32. Token ids and positions are int32;
- *    slots are int64.
+ *    states and KV caches use the config's storage dtype: bfloat16 (raw 16-bit bf16 values)
+ *    or fp32. Activations stay fp32 inside the library (a bf16 GEMM takes them as exact pairs
+ *    of bf16 halves); the block's q/k/v are rounded to the storage type like cached K/V. The
+ *    RoPE table and hidden_out are fp32. Token ids and positions are int32; slots are int64.
  *  - Host-side validation covers pointers and scalars only; a failing call returns a negative
  *    status, enqueues nothing, and dflash_last_error() (thread-local) explains it. Values in
  *    device memory (positions, sequence lengths, block tables, slots, token ids) are not
@@ -67,7 +68,7 @@ typedef struct dflash_config {
   int32_t block_size;     /* bs; K = bs - 1 drafts */
   int32_t mask_token_id;
   float rms_eps;
-  int32_t dtype;          /* dflash_dtype: storage type of weights, activations and KV */
+  int32_t dtype;          /* dflash_dtype: storage type of weights, aux states and KV */
 } dflash_config;
 
 /* Drafter weights. Single tensors are device pointers; per-layer tensors are host arrays of
@@ -159,14 +160,14 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
  * argmax (lowest index on ties) gives the drafts.
  *   seq_lens: device [batch] int32, clamped to [0, max_context].  bonus_tokens: device
  *   [batch], clamped to [0, V).  Outputs: draft_token_ids [batch, bs] = [bonus, drafts],
- *   drafts_only [batch, K], and optionally hidden_out [batch*K, H] (storage dtype): the
+ *   drafts_only [batch, K], and optionally hidden_out [batch*K, H] (fp32): the
  *   final-norm rows fed to the LM head (NULL skips it).
  * batch == 0 returns DFLASH_OK and does nothing. */
 dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weights *w,
                                    const dflash_kv_cache *cache, int32_t batch,
                                    const int32_t *bonus_tokens, const int32_t *seq_lens,
                                    int32_t max_context, int32_t *draft_token_ids,
-                                   int32_t *drafts_only, void *hidden_out, void *workspace,
+                                   int32_t *drafts_only, float *hidden_out, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
 /* Greedy verification ([N] "Async Rejection and Position Correction": rejected entries are

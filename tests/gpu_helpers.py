@@ -89,7 +89,7 @@ class Setup:
         spec = self.spec
         bonus_d = torch.from_numpy(np.asarray(bonus, np.int32)).cuda()
         ctx_d = torch.from_numpy(self.ctx).cuda()
-        hid = torch.empty((self.B * (spec.block_size - 1), spec.hidden), dtype=binding.storage_dtype(spec),
+        hid = torch.empty((self.B * (spec.block_size - 1), spec.hidden), dtype=torch.float32,
                           device="cuda") if hidden else None
         ids, drafts = self.dev.propose(self.cache, bonus_d, ctx_d, self.max_ctx, self.ws_prop, hidden_out=hid)
         torch.cuda.synchronize()
@@ -110,3 +110,31 @@ class Setup:
                 pos = np.arange(r0, r0 + n)
                 O.inject_context_kv(spec, Wn, kc, vc, aux, pos, self.slots(b, pos), mode_of(spec))
         return kc, vc
+
+
+def oracle_cache_local(st, seqs, Wn):
+    """Oracle caches holding only the sequences `seqs`, on a compact local page table.
+    Returns (k_cache, v_cache, local_block_table) with row i of the table serving seqs[i]."""
+    spec, P = st.spec, st.P
+    maxb = st.bt.shape[1]
+    bt = np.arange(len(seqs) * maxb, dtype=np.int32).reshape(len(seqs), maxb)
+    shape = (len(seqs) * maxb, P, spec.n_kv_heads, spec.head_dim)
+    kc = [np.zeros(shape, np.float32) for _ in range(spec.n_layers)]
+    vc = [np.zeros(shape, np.float32) for _ in range(spec.n_layers)]
+    for i, b in enumerate(seqs):
+        c = int(st.ctx[b])
+        for r0 in range(0, c, 2048):
+            n = min(2048, c - r0)
+            aux = [synth.as_f32(a) for a in synth.aux_states_fast(spec, st.seed, b, r0, n)]
+            pos = np.arange(r0, r0 + n)
+            O.inject_context_kv(spec, Wn, kc, vc, aux, pos, O.paged_slots(bt, np.full(n, i), pos, P), mode_of(spec))
+    return kc, vc, bt
+
+
+def gpu_cache_rows(st, b, rows):
+    """The GPU cache entries (K, V per layer) of sequence b at positions `rows`."""
+    spec = st.spec
+    sl = st.slots(b, np.asarray(rows))
+    ks = [t.view(-1, spec.n_kv_heads, spec.head_dim)[torch.from_numpy(sl).cuda()].float().cpu().numpy() for t in st.cache.k]
+    vs = [t.view(-1, spec.n_kv_heads, spec.head_dim)[torch.from_numpy(sl).cuda()].float().cpu().numpy() for t in st.cache.v]
+    return ks, vs
