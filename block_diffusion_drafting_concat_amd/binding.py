@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.dflash_profile_enable.argtypes = [_i32]
         L.dflash_profile_enable.restype = _i32
         L.dflash_profile_collect.restype = _i32
+        L.dflash_profile_filter.argtypes = [ctypes.c_char_p]
+        L.dflash_profile_filter.restype = _i32
         L.dflash_profile_count.restype = _i32
         L.dflash_profile_entry.argtypes = [_i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
                                            ctypes.POINTER(ctypes.c_double)]
@@ -231,6 +233,11 @@ class Drafter:
 
 def profile_enable(on: bool) -> None:
     _check(lib().dflash_profile_enable(1 if on else 0))
+
+
+def profile_filter(names=None) -> None:
+    """Time only the launches of these kernel names (None: every launch)."""
+    _check(lib().dflash_profile_filter(",".join(names).encode() if names else None))
 
 
 def profile_reset() -> None:

@@ -89,22 +89,34 @@ struct Carver {
 
 constexpr int kInjectChunk = 4096;  // rows per injection pass
 
+// Output tiles of a GEMM (one split-K counter each) and its fp32 partial buffer size.
+int gemm_tiles(int M, int N, int D, GemmEpi e) { return gemm_col_groups(M, N, D, e) * gemm_row_blocks(M); }
+size_t gemm_part_floats(int splits, int M, int N, GemmEpi e) {
+  return splits > 1 ? (size_t)splits * M * N * (e == GemmEpi::kSwiGLU ? 2 : 1) : 0;
+}
+
 struct InjectPlan {
-  int rows, s_fc, s_kv;
-  size_t off_part, off_ctx, total;
+  int rows, s_fc, s_kv, ss_groups, n_ctr;
+  size_t off_y, off_ss, off_part, off_ctr, total;
 };
 
 InjectPlan plan_inject(const dflash_config *c, int rows) {
   InjectPlan p{};
   p.rows = rows;
   const bool bf = is_bf16(c);
-  const int kvn = c->n_layers * 2 * c->n_kv_heads * c->head_dim;
-  p.s_fc = gemm_plan_splits(rows, c->hidden, c->n_aux * c->target_hidden, bf, GemmEpi::kStore);
-  p.s_kv = gemm_plan_splits(rows, std::max(kvn, 16), c->hidden, bf, GemmEpi::kStore);
-  const size_t part = std::max((size_t)p.s_fc * c->hidden, (size_t)p.s_kv * kvn) * rows * sizeof(float);
+  const int H = c->hidden, D = c->head_dim;
+  const int kvn = c->n_layers * 2 * c->n_kv_heads * D;
+  p.s_fc = gemm_plan_splits(rows, H, c->n_aux * c->target_hidden, D, bf, GemmEpi::kStore);
+  p.s_kv = gemm_plan_splits(rows, std::max(kvn, 16), H, D, bf, GemmEpi::kKvScatter);
+  p.ss_groups = gemm_col_groups(rows, H, D, GemmEpi::kStore);
+  p.n_ctr = std::max(gemm_tiles(rows, H, D, GemmEpi::kStore), gemm_tiles(rows, std::max(kvn, 16), D, GemmEpi::kKvScatter));
+  const size_t part = std::max(gemm_part_floats(p.s_fc, rows, H, GemmEpi::kStore),
+                               gemm_part_floats(p.s_kv, rows, kvn, GemmEpi::kKvScatter));
   Carver cv;
-  p.off_part = cv.take(part);
-  p.off_ctx = cv.take((size_t)rows * c->hidden * sizeof(float));
+  p.off_y = cv.take((size_t)rows * H * sizeof(float));
+  p.off_ss = cv.take((size_t)p.ss_groups * rows * sizeof(float));
+  p.off_part = cv.take(part * sizeof(float));
+  p.off_ctr = cv.take((size_t)p.n_ctr * sizeof(unsigned));
   p.total = cv.off;
   return p;
 }
@@ -112,8 +124,8 @@ InjectPlan plan_inject(const dflash_config *c, int rows) {
 struct ProposePlan {
   int B, M, Mk;
   int s_qkv, s_o, s_gu, s_down;
-  int chunk, nsplit, lm_groups;
-  size_t off_x, off_h, off_part, off_q, off_k, off_v, off_o, off_act, off_f, off_po, off_pm, off_pl, off_amv,
+  int chunk, nsplit, lm_groups, ss_groups, n_ctr;
+  size_t off_x, off_ss, off_part, off_ctr, off_q, off_k, off_v, off_o, off_act, off_po, off_pm, off_pl, off_amv,
       off_ami, total;
 };
 
@@ -125,28 +137,32 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
   p.B = B;
   p.M = B * c->block_size;
   p.Mk = B * K;
+  const int M = p.M;
   const int nqkv = (QH + 2 * KVH) * D;
-  p.s_qkv = gemm_plan_splits(p.M, nqkv, H, bf, GemmEpi::kStore);
-  p.s_o = gemm_plan_splits(p.M, H, QH * D, bf, GemmEpi::kResidAdd);
-  p.s_gu = gemm_plan_splits(p.M, I, H, bf, GemmEpi::kSwiGLU);
-  p.s_down = gemm_plan_splits(p.M, H, I, bf, GemmEpi::kResidAdd);
+  p.s_qkv = gemm_plan_splits(M, nqkv, H, D, bf, GemmEpi::kHeadNormRope);
+  p.s_o = gemm_plan_splits(M, H, QH * D, D, bf, GemmEpi::kResidAdd);
+  p.s_gu = gemm_plan_splits(M, I, H, D, bf, GemmEpi::kSwiGLU);
+  p.s_down = gemm_plan_splits(M, H, I, D, bf, GemmEpi::kResidAdd);
   attn_plan(B, KVH, max_ctx + c->block_size, &p.chunk, &p.nsplit);
-  p.lm_groups = gemm_col_groups(p.Mk, c->vocab, GemmEpi::kArgmax);
+  p.lm_groups = gemm_col_groups(p.Mk, c->vocab, D, GemmEpi::kArgmax);
+  p.ss_groups = gemm_col_groups(M, H, D, GemmEpi::kResidAdd);
+  p.n_ctr = std::max(std::max(gemm_tiles(M, nqkv, D, GemmEpi::kHeadNormRope), gemm_tiles(M, H, D, GemmEpi::kResidAdd)),
+                     gemm_tiles(M, I, D, GemmEpi::kSwiGLU));
+  const size_t part = std::max(std::max(gemm_part_floats(p.s_qkv, M, nqkv, GemmEpi::kHeadNormRope),
+                                        gemm_part_floats(p.s_o, M, H, GemmEpi::kResidAdd)),
+                               std::max(gemm_part_floats(p.s_gu, M, I, GemmEpi::kSwiGLU),
+                                        gemm_part_floats(p.s_down, M, H, GemmEpi::kResidAdd)));
   const size_t es = elem_size(c);
-  // partials: QKV always (its consumer is the q/k norm kernel); the others only when split
-  const size_t part = std::max(std::max((size_t)p.s_qkv * nqkv, (size_t)(p.s_o > 1 ? p.s_o : 0) * H),
-                               std::max((size_t)(p.s_gu > 1 ? p.s_gu : 0) * 2 * I, (size_t)(p.s_down > 1 ? p.s_down : 0) * H)) *
-                      p.M * sizeof(float);
   Carver cv;
-  p.off_x = cv.take((size_t)p.M * H * sizeof(float));
-  p.off_h = cv.take((size_t)p.M * H * sizeof(float));
-  p.off_part = cv.take(part);
-  p.off_q = cv.take((size_t)p.M * QH * D * es);
-  p.off_k = cv.take((size_t)p.M * KVH * D * es);
-  p.off_v = cv.take((size_t)p.M * KVH * D * es);
-  p.off_o = cv.take((size_t)p.M * QH * D * sizeof(float));
-  p.off_act = cv.take((size_t)p.M * I * sizeof(float));
-  p.off_f = cv.take((size_t)std::max(p.Mk, 1) * H * sizeof(float));
+  p.off_x = cv.take((size_t)M * H * sizeof(float));
+  p.off_ss = cv.take((size_t)p.ss_groups * M * sizeof(float));
+  p.off_part = cv.take(part * sizeof(float));
+  p.off_ctr = cv.take((size_t)p.n_ctr * sizeof(unsigned));
+  p.off_q = cv.take((size_t)M * QH * D * es);
+  p.off_k = cv.take((size_t)M * KVH * D * es);
+  p.off_v = cv.take((size_t)M * KVH * D * es);
+  p.off_o = cv.take((size_t)M * QH * D * sizeof(float));
+  p.off_act = cv.take((size_t)M * I * sizeof(float));
   const size_t nrow = (size_t)B * KVH * p.nsplit * 64;
   p.off_po = cv.take(nrow * D * sizeof(float));
   p.off_pm = cv.take(nrow * sizeof(float));
@@ -182,18 +198,39 @@ dflash_status check_cache(const dflash_config *c, const dflash_kv_cache *kv) {
   return DFLASH_OK;
 }
 
-GemmArgs gemm_args(const char *tag, const void *a, int64_t lda, int M, int N, int K) {
+GemmArgs gemm_args(const dflash_config *c, const char *tag, const void *a, int64_t lda, int M, int N, int K,
+                   unsigned *counters, float *part) {
   GemmArgs g{};
   g.a[0] = a;
   g.a_nseg = 1;
   g.lda = lda;
+  g.a_f32 = true;  // activations are fp32; only the auxiliary states come in the storage type
   g.b_nseg = 1;
   g.M = M;
   g.N = N;
   g.K = K;
+  g.eps = c->rms_eps;
+  g.head_dim = c->head_dim;
+  g.n_q_heads = c->n_q_heads;
+  g.n_kv_heads = c->n_kv_heads;
+  g.block_size = c->block_size;
+  g.counters = counters;
+  g.part = part;
   g.tag = tag;
-  g.a_f32 = true;  // activations are fp32; only the auxiliary states are bf16
   return g;
+}
+
+void set_norm(GemmArgs &g, const void *w, const float *ss, int groups, int rows) {
+  g.norm_w = w;
+  g.ss = ss;
+  g.ss_groups = groups;
+  g.ss_rows = rows;
+}
+
+void set_rope(GemmArgs &g, const dflash_weights *w) {
+  g.rope_cos = w->rope_cos;
+  g.rope_sin = w->rope_sin;
+  g.rope_max_pos = w->rope_max_pos;
 }
 
 }  // namespace
@@ -290,50 +327,40 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
     if (p.total > workspace_bytes)
       return fail(DFLASH_ERR_WORKSPACE_TOO_SMALL, "inject needs %zu workspace bytes, got %zu", p.total,
                   workspace_bytes);
+    float *y = at<float>(workspace, p.off_y);
+    float *ss = at<float>(workspace, p.off_ss);
     float *part = at<float>(workspace, p.off_part);
-    float *ctx = at<float>(workspace, p.off_ctx);
+    unsigned *ctr = at<unsigned>(workspace, p.off_ctr);
+    HIP_TRY(launch_zero(ctr, p.n_ctr, s));  // each chunk's plan places the counters anew
 
     // fc over the concatenated auxiliary states, read in place from the n_aux pointers
-    GemmArgs g = gemm_args("gemm.fc", nullptr, aux_row_stride, rows, H, cfg->n_aux * cfg->target_hidden);
+    GemmArgs g = gemm_args(cfg, "gemm.fc", nullptr, aux_row_stride, rows, H, cfg->n_aux * cfg->target_hidden, ctr,
+                           part);
     for (int j = 0; j < cfg->n_aux; ++j)
       g.a[j] = static_cast<const char *>(aux[j]) + (size_t)r0 * aux_row_stride * es;
     g.a_nseg = cfg->n_aux;
     g.a_f32 = false;  // the auxiliary states come in the storage type
     g.b[0] = w->fc;
     g.b_end[0] = H;
-    g.out = part;
-    g.part = part;
+    g.out = y;
+    g.ss_out = ss;
     HIP_TRY(launch_gemm(g, bf, GemmEpi::kStore, p.s_fc, s));
-    // hidden_norm
-    HIP_TRY(launch_rmsnorm(bf, rows, H, nullptr, part, p.s_fc, w->hidden_norm, cfg->rms_eps, ctx, 0, nullptr, s));
-    // K/V of every layer in one projection
-    GemmArgs k = gemm_args("gemm.kv", ctx, H, rows, kvn, H);
+
+    // hidden_norm on load; K/V of every layer in one projection; k_norm + RoPE + scatter
+    GemmArgs k = gemm_args(cfg, "gemm.kv", y, H, rows, kvn, H, ctr, part);
+    set_norm(k, w->hidden_norm, ss, p.ss_groups, rows);
     k.b[0] = w->kv_fused;
     k.b_end[0] = kvn;
-    k.out = part;
-    k.part = part;
-    HIP_TRY(launch_gemm(k, bf, GemmEpi::kStore, p.s_kv, s));
-
-    KvScatterArgs a{};
-    a.N = rows;
-    a.L = cfg->n_layers;
-    a.KVH = cfg->n_kv_heads;
-    a.D = cfg->head_dim;
-    a.kv = part;
-    a.splits = p.s_kv;
+    set_rope(k, w);
     for (int l = 0; l < cfg->n_layers; ++l) {
-      a.k_norm[l] = w->k_norm[l];
-      a.k_cache[l] = cache->k[l];
-      a.v_cache[l] = cache->v[l];
+      k.layer_k_norm[l] = w->k_norm[l];
+      k.k_cache[l] = cache->k[l];
+      k.v_cache[l] = cache->v[l];
     }
-    a.eps = cfg->rms_eps;
-    a.rope_cos = w->rope_cos;
-    a.rope_sin = w->rope_sin;
-    a.rope_max_pos = w->rope_max_pos;
-    a.positions = positions + r0;
-    a.slot_mapping = slot_mapping + r0;
-    a.num_slots = (int64_t)cache->num_pages * cache->page_size;
-    HIP_TRY(launch_kv_scatter(bf, a, s));
+    k.positions = positions + r0;
+    k.slot_mapping = slot_mapping + r0;
+    k.num_slots = (int64_t)cache->num_pages * cache->page_size;
+    HIP_TRY(launch_gemm(k, bf, GemmEpi::kKvScatter, p.s_kv, s));
   }
   return ok();
 }
@@ -374,22 +401,22 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
   const int H = cfg->hidden, D = cfg->head_dim, QH = cfg->n_q_heads, KVH = cfg->n_kv_heads;
   const int I = cfg->intermediate, bs = cfg->block_size, K = bs - 1, M = p.M;
   float *x = at<float>(workspace, p.off_x);
-  float *h = at<float>(workspace, p.off_h);
+  float *ss = at<float>(workspace, p.off_ss);
   float *part = at<float>(workspace, p.off_part);
+  unsigned *ctr = at<unsigned>(workspace, p.off_ctr);
   void *q = at<char>(workspace, p.off_q);
   void *kb = at<char>(workspace, p.off_k);
   void *vb = at<char>(workspace, p.off_v);
   float *o = at<float>(workspace, p.off_o);
   float *act = at<float>(workspace, p.off_act);
-  float *f = at<float>(workspace, p.off_f);
 
-  HIP_TRY(launch_embed(bf, w->embed, cfg->vocab, H, bonus_tokens, batch, bs, cfg->mask_token_id, x, s));
-  int pending = 0;  // split count of down-projection partials not yet added to x
+  HIP_TRY(launch_embed(bf, w->embed, cfg->vocab, H, bonus_tokens, batch, bs, cfg->mask_token_id, x, ss, ctr, p.n_ctr,
+                       s));
+  int ss_groups = 1;  // column groups of the last producer of x (the embedding: one)
   for (int l = 0; l < L; ++l) {
-    HIP_TRY(launch_rmsnorm(bf, M, H, x, part, pending, w->in_norm[l], cfg->rms_eps, h, 0, nullptr, s));
-
-    // q | k | v in one pass over the three projections
-    GemmArgs g = gemm_args("gemm.qkv", h, H, M, (QH + 2 * KVH) * D, H);
+    // input_layernorm on load; q | k | v in one pass; q/k norm + RoPE in the epilogue
+    GemmArgs g = gemm_args(cfg, "gemm.qkv", x, H, M, (QH + 2 * KVH) * D, H, ctr, part);
+    set_norm(g, w->in_norm[l], ss, ss_groups, M);
     g.b[0] = w->wq[l];
     g.b[1] = w->wk[l];
     g.b[2] = w->wv[l];
@@ -397,11 +424,15 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     g.b_end[1] = (QH + KVH) * D;
     g.b_end[2] = (QH + 2 * KVH) * D;
     g.b_nseg = 3;
-    g.out = part;
-    g.part = part;
-    HIP_TRY(launch_gemm(g, bf, GemmEpi::kStore, p.s_qkv, s));
-    HIP_TRY(launch_qk_norm_rope(bf, M, bs, QH, KVH, D, part, p.s_qkv, w->q_norm[l], w->k_norm[l], cfg->rms_eps,
-                                w->rope_cos, w->rope_sin, w->rope_max_pos, seq_lens, max_context, q, kb, vb, s));
+    g.q_norm = w->q_norm[l];
+    g.k_norm = w->k_norm[l];
+    g.seq_lens = seq_lens;
+    g.max_ctx = max_context;
+    set_rope(g, w);
+    g.q = q;
+    g.k = kb;
+    g.v = vb;
+    HIP_TRY(launch_gemm(g, bf, GemmEpi::kHeadNormRope, p.s_qkv, s));
 
     AttnArgs at_{};
     at_.q = q;
@@ -428,40 +459,39 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     at_.o = o;
     HIP_TRY(launch_attention(bf, at_, s));
 
-    // O projection: residual add in place, or split partials summed by the post-norm
-    GemmArgs go = gemm_args("gemm.o", o, QH * D, M, H, QH * D);
+    // O projection + residual add; the row sums of squares feed the post-attention norm
+    GemmArgs go = gemm_args(cfg, "gemm.o", o, QH * D, M, H, QH * D, ctr, part);
     go.b[0] = w->wo[l];
     go.b_end[0] = H;
     go.out = x;
-    go.part = part;
+    go.ss_out = ss;
     HIP_TRY(launch_gemm(go, bf, GemmEpi::kResidAdd, p.s_o, s));
-    HIP_TRY(launch_rmsnorm(bf, M, H, x, part, p.s_o > 1 ? p.s_o : 0, w->post_norm[l], cfg->rms_eps, h, 0, nullptr,
-                           s));
+    ss_groups = p.ss_groups;
 
-    // gate | up with SwiGLU (in place when unsplit)
-    GemmArgs gu = gemm_args("gemm.gate_up", h, H, M, I, H);
+    // post_attention_layernorm on load; gate | up with SwiGLU
+    GemmArgs gu = gemm_args(cfg, "gemm.gate_up", x, H, M, I, H, ctr, part);
+    set_norm(gu, w->post_norm[l], ss, ss_groups, M);
     gu.b[0] = w->w_gate[l];
     gu.b[1] = w->w_up[l];
     gu.b_end[0] = I;
     gu.b_end[1] = I;
     gu.b_nseg = 2;
-    gu.act = act;
-    gu.part = part;
+    gu.out = act;
     HIP_TRY(launch_gemm(gu, bf, GemmEpi::kSwiGLU, p.s_gu, s));
-    if (p.s_gu > 1) HIP_TRY(launch_swiglu(bf, M, I, part, p.s_gu, act, s));
 
-    GemmArgs gd = gemm_args("gemm.down", act, I, M, H, I);
+    GemmArgs gd = gemm_args(cfg, "gemm.down", act, I, M, H, I, ctr, part);
     gd.b[0] = w->w_down[l];
     gd.b_end[0] = H;
     gd.out = x;
-    gd.part = part;
+    gd.ss_out = ss;
     HIP_TRY(launch_gemm(gd, bf, GemmEpi::kResidAdd, p.s_down, s));
-    pending = p.s_down > 1 ? p.s_down : 0;
   }
-  // final norm on the drafted rows (block slots 1..K), compacted to [B*K, H]
-  HIP_TRY(launch_rmsnorm(bf, M, H, x, part, pending, w->final_norm, cfg->rms_eps, f, bs, hidden_out, s));
 
-  GemmArgs gl = gemm_args("gemm.lm_head", f, H, p.Mk, cfg->vocab, H);
+  // final norm on load over the drafted rows (block slots 1..K); LM head + per-group argmax
+  GemmArgs gl = gemm_args(cfg, "gemm.lm_head", x, H, p.Mk, cfg->vocab, H, ctr, part);
+  set_norm(gl, w->final_norm, ss, ss_groups, M);
+  gl.keep_bs = bs;
+  gl.a_out = hidden_out;
   gl.b[0] = w->lm_head;
   gl.b_end[0] = cfg->vocab;
   gl.amax_val = at<float>(workspace, p.off_amv);

@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <string>
 #include <vector>
 
 #include "../../include/dflash.h"
@@ -29,6 +30,15 @@ std::mutex g_mu;
 std::vector<Pending> g_pending;
 std::vector<Total> g_totals;
 std::vector<hipEvent_t> g_free;
+std::vector<std::string> g_filter;  // empty: every launch
+
+bool selected(const char *name) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_filter.empty()) return true;
+  for (const std::string &f : g_filter)
+    if (f == name) return true;
+  return false;
+}
 
 hipEvent_t take_event() {
   std::lock_guard<std::mutex> lk(g_mu);
@@ -47,7 +57,7 @@ hipEvent_t take_event() {
 bool profile_enabled() { return g_enabled.load(std::memory_order_relaxed); }
 
 ProfScope::ProfScope(const char *name, hipStream_t stream) : name_(name), stream_(stream) {
-  if (!profile_enabled()) return;
+  if (!profile_enabled() || !selected(name)) return;
   start_ = take_event();
   if (start_ && hipEventRecord(start_, stream_) != hipSuccess) start_ = nullptr;
 }
@@ -68,6 +78,23 @@ extern "C" {
 
 dflash_status dflash_profile_enable(int32_t on) {
   g_enabled.store(on != 0);
+  return DFLASH_OK;
+}
+
+dflash_status dflash_profile_filter(const char *names) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_filter.clear();
+  if (!names) return DFLASH_OK;
+  std::string cur;
+  for (const char *c = names;; ++c) {
+    if (*c == ',' || *c == '\0') {
+      if (!cur.empty()) g_filter.push_back(cur);
+      cur.clear();
+      if (*c == '\0') break;
+    } else {
+      cur += *c;
+    }
+  }
   return DFLASH_OK;
 }
 

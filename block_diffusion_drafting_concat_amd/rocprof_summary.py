@@ -21,7 +21,7 @@ from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEMM_SOURCES = ("block_diffusion_drafting_concat_amd/csrc/gemm.hip", "block_diffusion_drafting_concat_amd/csrc/common.h")
-EPI = {"0": "kStore", "1": "kResidAdd", "2": "kSwiGLU", "3": "kArgmax"}
+EPI = {"0": "kStore", "1": "kResidAdd", "2": "kSwiGLU", "3": "kArgmax", "4": "kHeadNormRope", "5": "kKvScatter"}
 COPY_BYTES = 1 << 30
 
 
@@ -34,13 +34,16 @@ def source_sha(paths=GEMM_SOURCES) -> str:
 
 
 def short_name(name: str) -> str:
-    """'gemm_kernel<unsigned short, 1, 8, 1, (dflash::GemmEpi)3, false>(...)' ->
-    'gemm_kernel<bf16,MT=1,CW=8,KW=1,kArgmax>'; other kernels: the name without arguments."""
-    m = re.search(r"gemm_kernel<([^,]+), (\d+), (\d+), (\d+), \(dflash::GemmEpi\)(\d), (true|false)>", name)
+    """'gemm_kernel<unsigned short, 1, 8, 1, (dflash::GemmEpi)3, false, true>(...)' ->
+    'gemm_kernel<bf16,MT=1,CW=8,KW=1,kArgmax,fp32-A>'; other kernels: the name without
+    arguments."""
+    m = re.search(r"gemm_kernel<([^,]+), (\d+), (\d+), (\d+), \(dflash::GemmEpi\)(\d), (true|false), (true|false)>",
+                  name)
     if m:
         dt = "bf16" if "short" in m.group(1) else "f32"
         s = f"gemm_kernel<{dt},MT={m.group(2)},CW={m.group(3)},KW={m.group(4)},{EPI[m.group(5)]}"
-        return s + (",multi-A>" if m.group(6) == "true" else ">")
+        s += ",multi-A" if m.group(6) == "true" else ""
+        return s + (",fp32-A>" if m.group(7) == "true" else ">")
     name = re.sub(r"^void ", "", name)
     name = name.replace("dflash::(anonymous namespace)::", "")
     return re.sub(r"\(.*$", "", name)

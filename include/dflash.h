@@ -190,6 +190,10 @@ dflash_status dflash_greedy_verify(int32_t batch, int32_t num_drafts,
  * thread-safe. Enabling creates events (host-side runtime objects); the drafting calls still
  * allocate no device memory. */
 dflash_status dflash_profile_enable(int32_t on);
+/* Restricts the timing to launches whose kernel name is in `names` (comma-separated, copied),
+ * so that a timed loop carries events only around the kernels of interest. NULL or ""
+ * times every launch (the default). */
+dflash_status dflash_profile_filter(const char *names);
 dflash_status dflash_profile_collect(void);
 void dflash_profile_reset(void);
 int32_t dflash_profile_count(void); /* number of distinct kernel names with totals */
