@@ -30,12 +30,13 @@ from block_diffusion_drafting_concat_amd import binding, synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 # GEMM kernel instances (by epilogue) and the profiling tags of their launches in a step.
 GEMM_KERNELS = {
-    "gemm_kernel<bf16,MT=1,CW=8,KW=1,kHeadNormRope,fp32-A>": ("gemm.qkv",),
-    "gemm_kernel<bf16,MT=1,CW=4,KW=2,kResidAdd,fp32-A>": ("gemm.o", "gemm.down"),
-    "gemm_kernel<bf16,MT=1,CW=4,KW=2,kSwiGLU,fp32-A>": ("gemm.gate_up",),
-    "gemm_kernel<bf16,MT=1,CW=8,KW=1,kArgmax,fp32-A>": ("gemm.lm_head",),
-    "gemm_kernel<bf16,MT=1,CW=4,KW=2,kStore,multi-A>": ("gemm.fc",),
-    "gemm_kernel<bf16,MT=1,CW=8,KW=1,kKvScatter,fp32-A>": ("gemm.kv",),
+    "gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=1,NCG=1,kHeadNormRope,fp32-A>": ("gemm.qkv",),
+    "gemm_kernel<bf16,MT=1,CW=4,CT=1,KW=2,NCG=1,kResidAdd,fp32-A>": ("gemm.o",),
+    "gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=1,NCG=1,kResidAdd,fp32-A>": ("gemm.down",),
+    "gemm_kernel<bf16,MT=1,CW=4,CT=1,KW=1,NCG=1,kSwiGLU,fp32-A>": ("gemm.gate_up",),
+    "gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=1,NCG=8,kArgmax,fp32-A>": ("gemm.lm_head",),
+    "gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=2,NCG=1,kStore,multi-A>": ("gemm.fc",),
+    "gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=1,NCG=1,kKvScatter,fp32-A>": ("gemm.kv",),
 }
 GEMM_SOURCES = ("block_diffusion_drafting_concat_amd/csrc/gemm.hip", "block_diffusion_drafting_concat_amd/csrc/common.h")
 

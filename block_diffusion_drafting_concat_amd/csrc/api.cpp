@@ -89,14 +89,15 @@ struct Carver {
 
 constexpr int kInjectChunk = 4096;  // rows per injection pass
 
-// Output tiles of a GEMM (one split-K counter each) and its fp32 partial buffer size.
-int gemm_tiles(int M, int N, int D, GemmEpi e) { return gemm_col_groups(M, N, D, e) * gemm_row_blocks(M); }
-size_t gemm_part_floats(int splits, int M, int N, GemmEpi e) {
-  return splits > 1 ? (size_t)splits * M * N * (e == GemmEpi::kSwiGLU ? 2 : 1) : 0;
+// fp32 partial buffer of a GEMM (split-K only).
+size_t gemm_part_floats(const GemmPlan &p, int M, int N, GemmEpi e) {
+  return p.splits > 1 ? (size_t)p.splits * M * N * (e == GemmEpi::kSwiGLU ? 2 : 1) : 0;
 }
+int gemm_tiles(const GemmPlan &p) { return p.col_groups * p.row_blocks; }
 
 struct InjectPlan {
-  int rows, s_fc, s_kv, ss_groups, n_ctr;
+  int rows, n_ctr;
+  GemmPlan fc, kv;
   size_t off_y, off_ss, off_part, off_ctr, total;
 };
 
@@ -105,16 +106,15 @@ InjectPlan plan_inject(const dflash_config *c, int rows) {
   p.rows = rows;
   const bool bf = is_bf16(c);
   const int H = c->hidden, D = c->head_dim;
-  const int kvn = c->n_layers * 2 * c->n_kv_heads * D;
-  p.s_fc = gemm_plan_splits(rows, H, c->n_aux * c->target_hidden, D, bf, GemmEpi::kStore);
-  p.s_kv = gemm_plan_splits(rows, std::max(kvn, 16), H, D, bf, GemmEpi::kKvScatter);
-  p.ss_groups = gemm_col_groups(rows, H, D, GemmEpi::kStore);
-  p.n_ctr = std::max(gemm_tiles(rows, H, D, GemmEpi::kStore), gemm_tiles(rows, std::max(kvn, 16), D, GemmEpi::kKvScatter));
-  const size_t part = std::max(gemm_part_floats(p.s_fc, rows, H, GemmEpi::kStore),
-                               gemm_part_floats(p.s_kv, rows, kvn, GemmEpi::kKvScatter));
+  const int kvn = std::max(c->n_layers * 2 * c->n_kv_heads * D, 16);
+  p.fc = gemm_plan(rows, H, c->n_aux * c->target_hidden, D, bf, GemmEpi::kStore, c->n_aux > 1);
+  p.kv = gemm_plan(rows, kvn, H, D, bf, GemmEpi::kKvScatter, false);
+  p.n_ctr = std::max(gemm_tiles(p.fc), gemm_tiles(p.kv));
+  const size_t part = std::max(gemm_part_floats(p.fc, rows, H, GemmEpi::kStore),
+                               gemm_part_floats(p.kv, rows, kvn, GemmEpi::kKvScatter));
   Carver cv;
   p.off_y = cv.take((size_t)rows * H * sizeof(float));
-  p.off_ss = cv.take((size_t)p.ss_groups * rows * sizeof(float));
+  p.off_ss = cv.take((size_t)p.fc.col_groups * rows * sizeof(float));
   p.off_part = cv.take(part * sizeof(float));
   p.off_ctr = cv.take((size_t)p.n_ctr * sizeof(unsigned));
   p.total = cv.off;
@@ -123,8 +123,8 @@ InjectPlan plan_inject(const dflash_config *c, int rows) {
 
 struct ProposePlan {
   int B, M, Mk;
-  int s_qkv, s_o, s_gu, s_down;
-  int chunk, nsplit, lm_groups, ss_groups, n_ctr;
+  GemmPlan qkv, o, gu, down, lm;
+  int chunk, nsplit, n_ctr;
   size_t off_x, off_ss, off_part, off_ctr, off_q, off_k, off_v, off_o, off_act, off_po, off_pm, off_pl, off_amv,
       off_ami, total;
 };
@@ -139,23 +139,24 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
   p.Mk = B * K;
   const int M = p.M;
   const int nqkv = (QH + 2 * KVH) * D;
-  p.s_qkv = gemm_plan_splits(M, nqkv, H, D, bf, GemmEpi::kHeadNormRope);
-  p.s_o = gemm_plan_splits(M, H, QH * D, D, bf, GemmEpi::kResidAdd);
-  p.s_gu = gemm_plan_splits(M, I, H, D, bf, GemmEpi::kSwiGLU);
-  p.s_down = gemm_plan_splits(M, H, I, D, bf, GemmEpi::kResidAdd);
+  p.qkv = gemm_plan(M, nqkv, H, D, bf, GemmEpi::kHeadNormRope, false);
+  p.o = gemm_plan(M, H, QH * D, D, bf, GemmEpi::kResidAdd, false);
+  p.gu = gemm_plan(M, I, H, D, bf, GemmEpi::kSwiGLU, false);
+  p.down = gemm_plan(M, H, I, D, bf, GemmEpi::kResidAdd, false);
+  p.lm = gemm_plan(std::max(p.Mk, 1), c->vocab, H, D, bf, GemmEpi::kArgmax, false);
   attn_plan(B, KVH, max_ctx + c->block_size, &p.chunk, &p.nsplit);
-  p.lm_groups = gemm_col_groups(p.Mk, c->vocab, D, GemmEpi::kArgmax);
-  p.ss_groups = gemm_col_groups(M, H, D, GemmEpi::kResidAdd);
-  p.n_ctr = std::max(std::max(gemm_tiles(M, nqkv, D, GemmEpi::kHeadNormRope), gemm_tiles(M, H, D, GemmEpi::kResidAdd)),
-                     gemm_tiles(M, I, D, GemmEpi::kSwiGLU));
-  const size_t part = std::max(std::max(gemm_part_floats(p.s_qkv, M, nqkv, GemmEpi::kHeadNormRope),
-                                        gemm_part_floats(p.s_o, M, H, GemmEpi::kResidAdd)),
-                               std::max(gemm_part_floats(p.s_gu, M, I, GemmEpi::kSwiGLU),
-                                        gemm_part_floats(p.s_down, M, H, GemmEpi::kResidAdd)));
+  p.n_ctr = std::max(std::max(gemm_tiles(p.qkv), gemm_tiles(p.o)), std::max(gemm_tiles(p.gu), gemm_tiles(p.down)));
+  const size_t part = std::max(std::max(gemm_part_floats(p.qkv, M, nqkv, GemmEpi::kHeadNormRope),
+                                        gemm_part_floats(p.o, M, H, GemmEpi::kResidAdd)),
+                               std::max(gemm_part_floats(p.gu, M, I, GemmEpi::kSwiGLU),
+                                        gemm_part_floats(p.down, M, H, GemmEpi::kResidAdd)));
+  // the residual-stream producers (O and down projections) write one sum of squares per
+  // column group; the embedding writes one
+  const int ss_groups = std::max(std::max(p.o.col_groups, p.down.col_groups), 1);
   const size_t es = elem_size(c);
   Carver cv;
   p.off_x = cv.take((size_t)M * H * sizeof(float));
-  p.off_ss = cv.take((size_t)p.ss_groups * M * sizeof(float));
+  p.off_ss = cv.take((size_t)ss_groups * M * sizeof(float));
   p.off_part = cv.take(part * sizeof(float));
   p.off_ctr = cv.take((size_t)p.n_ctr * sizeof(unsigned));
   p.off_q = cv.take((size_t)M * QH * D * es);
@@ -167,8 +168,8 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
   p.off_po = cv.take(nrow * D * sizeof(float));
   p.off_pm = cv.take(nrow * sizeof(float));
   p.off_pl = cv.take(nrow * sizeof(float));
-  p.off_amv = cv.take((size_t)p.lm_groups * std::max(p.Mk, 1) * sizeof(float));
-  p.off_ami = cv.take((size_t)p.lm_groups * std::max(p.Mk, 1) * sizeof(int32_t));
+  p.off_amv = cv.take((size_t)p.lm.col_groups * std::max(p.Mk, 1) * sizeof(float));
+  p.off_ami = cv.take((size_t)p.lm.col_groups * std::max(p.Mk, 1) * sizeof(int32_t));
   p.total = cv.off;
   return p;
 }
@@ -344,11 +345,11 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
     g.b_end[0] = H;
     g.out = y;
     g.ss_out = ss;
-    HIP_TRY(launch_gemm(g, bf, GemmEpi::kStore, p.s_fc, s));
+    HIP_TRY(launch_gemm(g, bf, GemmEpi::kStore, p.fc, s));
 
     // hidden_norm on load; K/V of every layer in one projection; k_norm + RoPE + scatter
     GemmArgs k = gemm_args(cfg, "gemm.kv", y, H, rows, kvn, H, ctr, part);
-    set_norm(k, w->hidden_norm, ss, p.ss_groups, rows);
+    set_norm(k, w->hidden_norm, ss, p.fc.col_groups, rows);
     k.b[0] = w->kv_fused;
     k.b_end[0] = kvn;
     set_rope(k, w);
@@ -360,7 +361,7 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
     k.positions = positions + r0;
     k.slot_mapping = slot_mapping + r0;
     k.num_slots = (int64_t)cache->num_pages * cache->page_size;
-    HIP_TRY(launch_gemm(k, bf, GemmEpi::kKvScatter, p.s_kv, s));
+    HIP_TRY(launch_gemm(k, bf, GemmEpi::kKvScatter, p.kv, s));
   }
   return ok();
 }
@@ -432,7 +433,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     g.q = q;
     g.k = kb;
     g.v = vb;
-    HIP_TRY(launch_gemm(g, bf, GemmEpi::kHeadNormRope, p.s_qkv, s));
+    HIP_TRY(launch_gemm(g, bf, GemmEpi::kHeadNormRope, p.qkv, s));
 
     AttnArgs at_{};
     at_.q = q;
@@ -465,8 +466,8 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     go.b_end[0] = H;
     go.out = x;
     go.ss_out = ss;
-    HIP_TRY(launch_gemm(go, bf, GemmEpi::kResidAdd, p.s_o, s));
-    ss_groups = p.ss_groups;
+    HIP_TRY(launch_gemm(go, bf, GemmEpi::kResidAdd, p.o, s));
+    ss_groups = p.o.col_groups;
 
     // post_attention_layernorm on load; gate | up with SwiGLU
     GemmArgs gu = gemm_args(cfg, "gemm.gate_up", x, H, M, I, H, ctr, part);
@@ -477,14 +478,15 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     gu.b_end[1] = I;
     gu.b_nseg = 2;
     gu.out = act;
-    HIP_TRY(launch_gemm(gu, bf, GemmEpi::kSwiGLU, p.s_gu, s));
+    HIP_TRY(launch_gemm(gu, bf, GemmEpi::kSwiGLU, p.gu, s));
 
     GemmArgs gd = gemm_args(cfg, "gemm.down", act, I, M, H, I, ctr, part);
     gd.b[0] = w->w_down[l];
     gd.b_end[0] = H;
     gd.out = x;
     gd.ss_out = ss;
-    HIP_TRY(launch_gemm(gd, bf, GemmEpi::kResidAdd, p.s_down, s));
+    HIP_TRY(launch_gemm(gd, bf, GemmEpi::kResidAdd, p.down, s));
+    ss_groups = p.down.col_groups;
   }
 
   // final norm on load over the drafted rows (block slots 1..K); LM head + per-group argmax
@@ -496,8 +498,8 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
   gl.b_end[0] = cfg->vocab;
   gl.amax_val = at<float>(workspace, p.off_amv);
   gl.amax_idx = at<int32_t>(workspace, p.off_ami);
-  HIP_TRY(launch_gemm(gl, bf, GemmEpi::kArgmax, 1, s));
-  HIP_TRY(launch_argmax_reduce(batch, K, p.lm_groups, gl.amax_val, gl.amax_idx, bonus_tokens, cfg->vocab,
+  HIP_TRY(launch_gemm(gl, bf, GemmEpi::kArgmax, p.lm, s));
+  HIP_TRY(launch_argmax_reduce(batch, K, p.lm.col_groups, gl.amax_val, gl.amax_idx, bonus_tokens, cfg->vocab,
                                draft_token_ids, drafts_only, s));
   return ok();
 }

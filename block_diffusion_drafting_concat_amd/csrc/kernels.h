@@ -24,13 +24,13 @@ namespace dflash {
 // Split-K (`splits` > 1): every split writes its tile to part[s] ([M][NACC][N]) and the last
 // work-group of each output tile to arrive sums the splits in split order and runs the
 // epilogue. `counters` holds one zero-initialised counter per output tile
-// (gemm_col_groups * gemm_row_blocks); the reducing work-group resets it to zero.
+// (GemmPlan::col_groups * row_blocks); the reducing work-group resets it to zero.
 //
 // Epilogues on the final tile:
 //   kStore        out[m][n] = C                                  (fp32)
 //   kResidAdd     out[m][n] += C                                 (the fp32 residual stream)
 //   kSwiGLU       out[m][n] = silu(C_gate) * C_up, B = {gate [N,K], up [N,K]}
-//   kArgmax       amax_{val,idx}[m][col group] = (max, lowest index)   (no split)
+//   kArgmax       amax_{val,idx}[m][col group] = (max, lowest index)
 //   kHeadNormRope the block's q | k | v: per-head RMSNorm (q_norm / k_norm) and RoPE at
 //                 position min(seq_lens[b], max_ctx) + j on q and k, rounded to the storage
 //                 type into q [M][QH][D], k and v [M][KVH][D]; B = {wq, wk, wv}
@@ -86,11 +86,20 @@ struct GemmArgs {
 };
 
 int gemm_mt(int M);
-int gemm_col_groups(int M, int N, int head_dim, GemmEpi epi);  // column groups (argmax groups)
-int gemm_row_blocks(int M);
-// Split count for a (M, N, K) problem; shared by workspace planning and launch.
-int gemm_plan_splits(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi);
-hipError_t launch_gemm(const GemmArgs &g, bool bf16, GemmEpi epi, int splits, hipStream_t s);
+
+// Launch plan of one GEMM: work-group shape (cw wave columns x ct column tiles per wave x
+// kw K sub-slices), K splits, work-groups along the column groups (0: one per column
+// group; fewer: each loops over several), LDS bytes of one staged A pass. Deterministic in
+// its arguments, so the workspace planner and the launch agree.
+struct GemmPlan {
+  int cw, ct, kw;
+  int splits;
+  int grid_x;
+  int lds_budget;
+  int col_groups, row_blocks;  // output tiles = col_groups * row_blocks (split-K counters)
+};
+GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bool multi_a);
+hipError_t launch_gemm(const GemmArgs &g, bool bf16, GemmEpi epi, const GemmPlan &p, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------
 // Row-wise kernels

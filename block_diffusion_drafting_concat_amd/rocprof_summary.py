@@ -34,16 +34,17 @@ def source_sha(paths=GEMM_SOURCES) -> str:
 
 
 def short_name(name: str) -> str:
-    """'gemm_kernel<unsigned short, 1, 8, 1, (dflash::GemmEpi)3, false, true>(...)' ->
-    'gemm_kernel<bf16,MT=1,CW=8,KW=1,kArgmax,fp32-A>'; other kernels: the name without
-    arguments."""
-    m = re.search(r"gemm_kernel<([^,]+), (\d+), (\d+), (\d+), \(dflash::GemmEpi\)(\d), (true|false), (true|false)>",
-                  name)
+    """'gemm_kernel<unsigned short, 1, 8, 1, 1, 8, (dflash::GemmEpi)3, false, true>(...)' ->
+    'gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=1,NCG=8,kArgmax,fp32-A>'; other kernels: the name
+    without arguments."""
+    m = re.search(r"gemm_kernel<([^,]+), (\d+), (\d+), (\d+), (\d+), (\d+), \(dflash::GemmEpi\)(\d), "
+                  r"(true|false), (true|false)>", name)
     if m:
         dt = "bf16" if "short" in m.group(1) else "f32"
-        s = f"gemm_kernel<{dt},MT={m.group(2)},CW={m.group(3)},KW={m.group(4)},{EPI[m.group(5)]}"
-        s += ",multi-A" if m.group(6) == "true" else ""
-        return s + (",fp32-A>" if m.group(7) == "true" else ">")
+        s = (f"gemm_kernel<{dt},MT={m.group(2)},CW={m.group(3)},CT={m.group(4)},KW={m.group(5)},"
+             f"NCG={m.group(6)},{EPI[m.group(7)]}")
+        s += ",multi-A" if m.group(8) == "true" else ""
+        return s + (",fp32-A>" if m.group(9) == "true" else ">")
     name = re.sub(r"^void ", "", name)
     name = name.replace("dflash::(anonymous namespace)::", "")
     return re.sub(r"\(.*$", "", name)
