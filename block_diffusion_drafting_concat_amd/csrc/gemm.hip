@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kDefaultPassBytes = 60 << 10;  // LDS for one staged A pass unless the plan says more
 constexpr int kMaxLds = 160 << 10;           // LDS of one CU
-constexpr int kStageVecs = 4;                // A vectors staged per thread per round
+constexpr int kStageVecs = 2;                // A vectors staged per thread per round
 constexpr int kMaxGroupsPerWg = 8;           // column groups of one persistent work-group, max
 
 template <typename T>
@@ -59,8 +59,11 @@ __device__ __forceinline__ void head_norm_rope(float &x1, float &x2, bool own, i
   x2 = b * cs + a * sn;
 }
 
+// Occupancy at one row tile: 4-wave work-groups run four to a CU, 8-wave ones two (at most
+// 128 VGPRs); a work-group that owns several column groups keeps their accumulators and has
+// the CU alone.
 template <typename T, int MT, int CW, int CT, int KW, int NCG, GemmEpi E, bool kMultiA, bool kAF32>
-__global__ __launch_bounds__(CW *KW * 64) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG == 1 ? 2 : 1)) void gemm_kernel(GemmArgs g) {
   constexpr int NW = CW * KW, NT = NW * 64;
   constexpr int KPV = Storage<T>::kPerVec;
   constexpr int CH = ch_of<T>();
