@@ -5,6 +5,6 @@ The product path never imports it and shares no code with it.
 """
 from .dflash_oracle import (  # noqa: F401
     acceptance_metrics, apply_rope, attention, build_query_block, greedy_verify,
-    inject_context_kv, paged_slots, propose_block, rms_norm, round_bf16, round_f32,
-    storage_rounding,
+    inject_context_kv, paged_slots, prepare_proposal_inputs, propose_block, rms_norm, round_bf16,
+    round_f32, storage_rounding,
 )

@@ -316,3 +316,43 @@ def acceptance_metrics(accepted_len, num_drafts_per_block: int):
     return {"num_drafts": num_drafts, "num_draft_tokens": num_draft_tokens,
             "num_accepted_tokens": num_accepted, "acceptance_rate": rate,
             "acceptance_length": length}
+
+
+# --------------------------------------------------------------------------------------------
+# Proposal-input preparation ([N] "Async Rejection and Position Correction", "Paged KV
+# Integration", "Draft Block Construction")
+# --------------------------------------------------------------------------------------------
+def prepare_proposal_inputs(prev_out, vocab: int, opt_seq_lens, row_req, opt_positions, block_table,
+                            page_size: int):
+    """Corrects an optimistically scheduled step once the previous verification is known.
+
+    The scheduler prepared the step as if all K_prev drafts of the previous step had been
+    accepted. For each request b the previous rejection-sampler output prev_out[b] (K_prev + 1
+    entries: emitted tokens, -1 for rejected ones) gives
+      valid_b    = number of entries that are not -1 and lie below the vocabulary size,
+      rejected_b = (1 + K_prev) - valid_b,
+    and the step is corrected by removing the rejected positions:
+      seq_lens[b]   = opt_seq_lens[b] - rejected_b            (post-verification length)
+      positions[r]  = opt_positions[r] - rejected_{row_req[r]} (context rows to inject)
+      slots[r]      = paged slot of (row_req[r], positions[r])
+      bonus[b]      = the last valid entry of prev_out[b] (the block's slot-0 token).
+    A request with no valid entry keeps bonus 0, and a corrected position below 0 gets slot -1,
+    which injection skips (readings: neither arises from a consistent schedule, the greedy
+    rejection always emits at least one token)."""
+    prev = np.asarray(prev_out, dtype=np.int64)
+    B, K1 = prev.shape
+    ok = (prev != -1) & (prev >= 0) & (prev < vocab)
+    valid = ok.sum(axis=1)
+    rejected = K1 - valid
+    seq_lens = np.asarray(opt_seq_lens, dtype=np.int64) - rejected
+    req = np.asarray(row_req, dtype=np.int64)
+    positions = np.asarray(opt_positions, dtype=np.int64) - rejected[req]
+    slots = np.where(positions >= 0, paged_slots(block_table, req, np.maximum(positions, 0), page_size), -1)
+    bonus = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        idx = np.nonzero(ok[b])[0]
+        if idx.size:
+            bonus[b] = prev[b, idx[-1]]
+    return {"seq_lens": seq_lens.astype(np.int32), "positions": positions.astype(np.int32),
+            "slot_mapping": slots.astype(np.int64), "bonus": bonus.astype(np.int32),
+            "num_rejected": rejected.astype(np.int32)}
