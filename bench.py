@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """Throughput of the DFlash draft-proposal path on one MI355X.
 
-One step is the whole path on one batch: inject the step's new context rows into every draft
-layer's KV cache, propose one block per sequence, and greedily verify the drafts against
-synthetic target tokens. The default workload is the Qwen3-8B-shaped bf16 drafter at batch 1,
-block size 16 (15 drafts), a 2048-token context and 16 injected rows per step. Weights and
-inputs are seeded synthetic data, resident in HBM before timing starts.
+One step is the whole path on one batch: correct the proposal inputs on the device from the
+previous verification (positions, sequence lengths, cache slots, bonus tokens), inject the
+step's new context rows into every draft layer's KV cache, propose one block per sequence, and
+greedily verify the drafts against synthetic target tokens (acceptance counters fused). The
+default workload is the Qwen3-8B-shaped bf16 drafter at batch 1, block size 16 (15 drafts), a
+2048-token context and 16 injected rows per step. Weights and inputs are seeded synthetic data,
+resident in HBM before timing starts.
 
 Prints one JSON line (stdout): drafted tokens/s as `value`, draft blocks/s, the
 weight-streaming GEMM kernel's roofline, and the CPU oracle's rate on a bounded sample.
@@ -153,11 +155,35 @@ class Bench:
         self.vout = (torch.empty(self.B, dtype=torch.int32, device="cuda"),
                      torch.empty((self.B, K + 1), dtype=torch.int32, device="cuda"),
                      torch.empty(self.B, dtype=torch.int32, device="cuda"))
-        # synthetic target tokens from the drafts of a first step
+        self.stats = torch.zeros(3, dtype=torch.int64, device="cuda")
+        # Steady state. A first step (synthetic bonus) gives drafts, synthetic target tokens for
+        # them and the verification output. Every timed step then starts from that output as
+        # the previous step's result: the proposal inputs are corrected on the device from an
+        # optimistic schedule (all drafts accepted) back to the same context rows, so the
+        # workload is the same each step.
         self.target = torch.zeros((self.B, K + 1), dtype=torch.int32, device="cuda")
-        self.step()
+        self._plain_step()
         torch.cuda.synchronize()
         self.target = torch.from_numpy(synth.target_tokens(wl, self.out[1].cpu().numpy())).cuda()
+        self._plain_step()
+        torch.cuda.synchronize()
+        self.prev_out = self.vout[1].clone()
+        prev_bonus = self.vout[2].clone()
+        rejected = (K + 1 - self.vout[0]).to(torch.int32)
+        self.row_req = torch.from_numpy(np.repeat(np.arange(self.B), n).astype(np.int32)).cuda()
+        self.opt_seq = (self.seq_lens + rejected).to(torch.int32)
+        self.opt_pos = (self.step_pos + rejected[self.row_req.long()]).to(torch.int32)
+        self.bt_dev = torch.from_numpy(bt.astype(np.int32)).cuda()
+        self.prep = (torch.empty(self.B, dtype=torch.int32, device="cuda"),
+                     torch.empty(self.B * n, dtype=torch.int32, device="cuda"),
+                     torch.empty(self.B * n, dtype=torch.int64, device="cuda"),
+                     torch.empty(self.B, dtype=torch.int32, device="cuda"))
+        self.step()
+        torch.cuda.synchronize()
+        assert torch.equal(self.prep[0], self.seq_lens) and torch.equal(self.prep[1], self.step_pos)
+        assert torch.equal(self.prep[2], self.step_slots) and torch.equal(self.prep[3], prev_bonus)
+        self.target = torch.from_numpy(synth.target_tokens(wl, self.out[1].cpu().numpy())).cuda()
+        self.stats.zero_()
 
     def _inject_host(self, b, r0, n):
         aux = [a.cuda() for a in synth.aux_states_fast(self.spec, self.wl.seed, b, r0, n)]
@@ -166,10 +192,19 @@ class Bench:
         slots = (bt[b, np.minimum(pos // P, bt.shape[1] - 1)] * P + pos % P).astype(np.int64)
         self.dev.inject(self.cache, aux, torch.from_numpy(pos).cuda(), torch.from_numpy(slots).cuda(), self.ws_inj)
 
-    def step(self):
+    def _plain_step(self):
         self.dev.inject(self.cache, self.step_aux, self.step_pos, self.step_slots, self.ws_inj)
         self.dev.propose(self.cache, self.bonus, self.seq_lens, self.max_ctx, self.ws_prop, out=self.out)
         binding.verify(self.out[1], self.target, out=self.vout)
+
+    def step(self):
+        """One step of the path: correct the proposal inputs from the previous verification,
+        inject the context rows, propose one block, verify it (acceptance counters fused)."""
+        seq, pos, slots, bonus = binding.prepare(self.prev_out, self.spec.vocab, self.opt_seq, self.row_req,
+                                                 self.opt_pos, self.bt_dev, self.layout.page_size, out=self.prep)
+        self.dev.inject(self.cache, self.step_aux, pos, slots, self.ws_inj)
+        self.dev.propose(self.cache, bonus, seq, self.max_ctx, self.ws_prop, out=self.out)
+        binding.verify_with_stats(self.out[1], self.target, self.stats, out=self.vout)
 
     def timed(self, steps):
         torch.cuda.synchronize()
@@ -216,18 +251,19 @@ def cpu_baseline(bench: Bench):
                             mode)
     log(f"[bench] oracle prefill {c - n} rows in {time.time() - t0:.1f}s")
     aux = [synth.as_f32(a) for a in synth.aux_states(spec, wl.seed, b, c - n, n)]
-    pos = np.arange(c - n, c)
-    slots = O.paged_slots(bt, np.zeros(n, int), pos, lay.page_size)
-    bonus = bench.bonus.cpu().numpy()[:1]
+    prev_out = bench.prev_out.cpu().numpy()[:1]
+    opt_seq = bench.opt_seq.cpu().numpy()[:1]
+    opt_pos = bench.opt_pos.cpu().numpy()[:n]
     t0 = time.perf_counter()
-    O.inject_context_kv(spec, Wn, kc, vc, aux, pos, slots, mode)
-    res = O.propose_block(spec, Wn, kc, vc, bt, bonus, bench.ctx[:1], mode)
+    prep = O.prepare_proposal_inputs(prev_out, spec.vocab, opt_seq, np.zeros(n, int), opt_pos, bt, lay.page_size)
+    O.inject_context_kv(spec, Wn, kc, vc, aux, prep["positions"], prep["slot_mapping"], mode)
+    res = O.propose_block(spec, Wn, kc, vc, bt, prep["bonus"], prep["seq_lens"], mode)
     O.greedy_verify(res["drafts_only"], bench.target.cpu().numpy()[:1])
     dt = time.perf_counter() - t0
     K = spec.block_size - 1
     return {"value": K / dt, "unit": "drafted tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"1 step (inject {n} rows + propose + verify) of sequence 0 of {wl.name}, fp64 numpy",
-            "seconds_per_step": dt}
+            "sample": f"1 step (prepare + inject {n} rows + propose + verify) of sequence 0 of {wl.name}, "
+                      "fp64 numpy", "seconds_per_step": dt}
 
 
 def main():
@@ -239,6 +275,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one 1 GiB device copy (scale reference for rocprofv3 byte counters)")
+    ap.add_argument("--eager", action="store_true",
+                    help="report eager launches instead of replays of the captured step graph")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the drafting path of this build is "
@@ -289,24 +327,53 @@ def main():
     prof = binding.profile_collect()
     sec_plain = bench.timed(args.steps)  # the same steps with no event at all
 
+    # The step captured once as a hipGraph (the library enqueues kernels only: no allocation,
+    # no memset, no host synchronisation) and replayed; every replay must reproduce the eager
+    # step's drafts and verification.
+    sec_graph = None
+    if not args.eager:
+        ref = [t.clone() for t in (bench.out[0], bench.out[1], bench.vout[0], bench.vout[1])]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            bench.step()
+        for _ in range(3):
+            for t in (bench.out[0], bench.out[1], bench.vout[0], bench.vout[1]):
+                t.fill_(-7)
+            graph.replay()
+            torch.cuda.synchronize()
+            got = (bench.out[0], bench.out[1], bench.vout[0], bench.vout[1])
+            if not all(torch.equal(a, c) for a, c in zip(got, ref)):
+                raise SystemExit("graph replay differs from the eager step")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        sec_graph = (time.perf_counter() - t0) / args.steps
+
     if args.copy_calib:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    st = bench.stats.cpu().numpy().astype(float)
+    acceptance = {"num_drafts": int(st[0]), "num_draft_tokens": int(st[1]), "num_accepted_tokens": int(st[2]),
+                  "rate": st[2] / st[1] if st[1] else None, "length": 1 + st[2] / st[0] if st[0] else None,
+                  "note": "device counters fused into verify, on synthetic target tokens (a sanity check, not a "
+                          "model's acceptance)"}
     g_launch, g_ms, g_bytes = per_kernel_of(prof)[dom]
     achieved = g_bytes / (g_ms * 1e-3) / 1e9 if g_ms > 0 else 0.0
     traffic = load_traffic(dom, wl.name)
     sbytes = step_bytes(spec, B, bench.ctx, wl.inject_rows)
     result = {
         "metric": "drafted tokens/sec and draft blocks/sec (Qwen3-8B-shape, b16); % HBM/MFMA roofline",
-        "value": B * K / sec,
+        "value": B * K / (sec_graph if sec_graph else sec),
         "unit": "drafted tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": sec * 1e3,
+        "ms_per_step": (sec_graph if sec_graph else sec) * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -317,11 +384,15 @@ def main():
                    "hidden": spec.hidden, "layers": spec.n_layers, "heads": [spec.n_q_heads, spec.n_kv_heads],
                    "head_dim": spec.head_dim, "intermediate": spec.intermediate, "vocab": spec.vocab,
                    "fc_in": spec.n_aux * spec.target_hidden, "page_size": wl.page_size},
-        "draft_blocks_per_s": B / sec,
+        "draft_blocks_per_s": B / (sec_graph if sec_graph else sec),
+        "timing": "replays of the captured step graph" if sec_graph else "eager launches",
+        "ms_per_step_eager": sec * 1e3,
+        "acceptance": acceptance,
         "ms_per_step_without_events": sec_plain * 1e3,
         "launches_per_step": sum(v[0] for v in prof_all.values()) / n_prof,
-        "step_roofline": {"bound": "hbm", "algorithmic_bytes": sbytes, "achieved": sbytes / sec / 1e9,
-                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": sbytes / sec / 1e9 / HBM_PEAK_GBS},
+        "step_roofline": {"bound": "hbm", "algorithmic_bytes": sbytes,
+                          "achieved": sbytes / (sec_graph if sec_graph else sec) / 1e9, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": sbytes / (sec_graph if sec_graph else sec) / 1e9 / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "kernel": dom,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "launches": g_launch,

@@ -71,8 +71,12 @@ def lib() -> ctypes.CDLL:
         L.dflash_propose_block.argtypes = [P(Config), P(Weights), P(KvCache), _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                            _vp, ctypes.c_size_t, _vp]
         L.dflash_greedy_verify.argtypes = [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.dflash_greedy_verify_stats.argtypes = [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.dflash_prepare_proposal_inputs.argtypes = [_i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32,
+                                                     _vp, _vp, _vp, _vp, _vp]
         for fn in ("dflash_build_rope_table", "dflash_build_fused_kv_weight", "dflash_inject_context_kv",
-                   "dflash_propose_block", "dflash_greedy_verify"):
+                   "dflash_propose_block", "dflash_greedy_verify", "dflash_greedy_verify_stats",
+                   "dflash_prepare_proposal_inputs"):
             getattr(L, fn).restype = _i32
         L.dflash_profile_enable.argtypes = [_i32]
         L.dflash_profile_enable.restype = _i32
@@ -152,6 +156,22 @@ def greedy_verify(batch, num_drafts, draft_tokens, target_tokens, accepted_len, 
                   stream=None) -> None:
     _check(lib().dflash_greedy_verify(batch, num_drafts, _ptr(draft_tokens), _ptr(target_tokens),
                                       _ptr(accepted_len), _ptr(output_tokens), _ptr(next_bonus), _stream(stream)))
+
+
+def greedy_verify_stats(batch, num_drafts, draft_tokens, target_tokens, accepted_len, output_tokens, next_bonus,
+                        stats, stream=None) -> None:
+    _check(lib().dflash_greedy_verify_stats(batch, num_drafts, _ptr(draft_tokens), _ptr(target_tokens),
+                                            _ptr(accepted_len), _ptr(output_tokens), _ptr(next_bonus),
+                                            _ptr(stats), _stream(stream)))
+
+
+def prepare_proposal_inputs(batch, prev_num_drafts, prev_out, vocab, opt_seq_lens, n_rows, row_req, opt_positions,
+                            block_table, max_blocks_per_seq, page_size, seq_lens, positions, slot_mapping, bonus,
+                            stream=None) -> None:
+    _check(lib().dflash_prepare_proposal_inputs(batch, prev_num_drafts, _ptr(prev_out), vocab, _ptr(opt_seq_lens),
+                                                n_rows, _ptr(row_req), _ptr(opt_positions), _ptr(block_table),
+                                                max_blocks_per_seq, page_size, _ptr(seq_lens), _ptr(positions),
+                                                _ptr(slot_mapping), _ptr(bonus), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------------------
@@ -264,4 +284,30 @@ def verify(drafts, target, out=None, stream=None):
                torch.empty((B, K + 1), dtype=torch.int32, device=drafts.device),
                torch.empty(B, dtype=torch.int32, device=drafts.device))
     greedy_verify(B, K, drafts, target, out[0], out[1], out[2], stream)
+    return out
+
+
+def verify_with_stats(drafts, target, stats, out=None, stream=None):
+    """Greedy verification that also adds this call's acceptance counters to stats
+    (int64 [3]: num_drafts, num_draft_tokens, num_accepted_tokens)."""
+    B, K = drafts.shape
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=drafts.device),
+               torch.empty((B, K + 1), dtype=torch.int32, device=drafts.device),
+               torch.empty(B, dtype=torch.int32, device=drafts.device))
+    greedy_verify_stats(B, K, drafts, target, out[0], out[1], out[2], stats, stream)
+    return out
+
+
+def prepare(prev_out, vocab, opt_seq_lens, row_req, opt_positions, block_table, page_size, out=None, stream=None):
+    """Proposal-input preparation; returns (seq_lens [B], positions [n], slot_mapping [n] int64,
+    bonus [B])."""
+    B, K1 = prev_out.shape
+    n = int(row_req.shape[0])
+    dev = prev_out.device
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(n, dtype=torch.int32, device=dev),
+               torch.empty(n, dtype=torch.int64, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+    prepare_proposal_inputs(B, K1 - 1, prev_out, vocab, opt_seq_lens, n, row_req, opt_positions, block_table,
+                            int(block_table.shape[1]), page_size, out[0], out[1], out[2], out[3], stream)
     return out

@@ -504,9 +504,10 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
   return ok();
 }
 
-dflash_status dflash_greedy_verify(int32_t batch, int32_t num_drafts, const int32_t *draft_tokens,
-                                   const int32_t *target_tokens, int32_t *accepted_len, int32_t *output_tokens,
-                                   int32_t *next_bonus, void *stream) {
+namespace {
+dflash_status verify_impl(int32_t batch, int32_t num_drafts, const int32_t *draft_tokens,
+                          const int32_t *target_tokens, int32_t *accepted_len, int32_t *output_tokens,
+                          int32_t *next_bonus, int64_t *stats, void *stream) {
   if (batch < 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "batch < 0");
   if (num_drafts < 1 || num_drafts > 63)
     return fail(DFLASH_ERR_UNSUPPORTED, "num_drafts %d outside [1, 63]", num_drafts);
@@ -514,7 +515,63 @@ dflash_status dflash_greedy_verify(int32_t batch, int32_t num_drafts, const int3
   if (!draft_tokens || !target_tokens || !accepted_len || !output_tokens || !next_bonus)
     return fail(DFLASH_ERR_INVALID_ARGUMENT, "an input/output pointer is NULL");
   HIP_TRY(launch_verify(batch, num_drafts, draft_tokens, target_tokens, accepted_len, output_tokens, next_bonus,
-                        (hipStream_t)stream));
+                        stats, (hipStream_t)stream));
+  return ok();
+}
+}  // namespace
+
+dflash_status dflash_greedy_verify(int32_t batch, int32_t num_drafts, const int32_t *draft_tokens,
+                                   const int32_t *target_tokens, int32_t *accepted_len, int32_t *output_tokens,
+                                   int32_t *next_bonus, void *stream) {
+  return verify_impl(batch, num_drafts, draft_tokens, target_tokens, accepted_len, output_tokens, next_bonus,
+                     nullptr, stream);
+}
+
+dflash_status dflash_greedy_verify_stats(int32_t batch, int32_t num_drafts, const int32_t *draft_tokens,
+                                         const int32_t *target_tokens, int32_t *accepted_len,
+                                         int32_t *output_tokens, int32_t *next_bonus, int64_t *stats,
+                                         void *stream) {
+  if (!stats && batch > 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "stats is NULL");
+  return verify_impl(batch, num_drafts, draft_tokens, target_tokens, accepted_len, output_tokens, next_bonus,
+                     stats, stream);
+}
+
+dflash_status dflash_prepare_proposal_inputs(int32_t batch, int32_t prev_num_drafts, const int32_t *prev_out,
+                                             int32_t vocab, const int32_t *opt_seq_lens, int32_t n_rows,
+                                             const int32_t *row_req, const int32_t *opt_positions,
+                                             const int32_t *block_table, int32_t max_blocks_per_seq,
+                                             int32_t page_size, int32_t *seq_lens, int32_t *positions,
+                                             int64_t *slot_mapping, int32_t *bonus, void *stream) {
+  if (batch < 0 || n_rows < 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "batch or n_rows < 0");
+  if (prev_num_drafts < 0 || prev_num_drafts > 63)
+    return fail(DFLASH_ERR_UNSUPPORTED, "prev_num_drafts %d outside [0, 63]", prev_num_drafts);
+  if (vocab <= 0 || page_size <= 0 || max_blocks_per_seq <= 0)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "vocab, page_size and max_blocks_per_seq must be positive");
+  if (batch == 0) {
+    if (n_rows > 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "context rows without requests");
+    return ok();
+  }
+  if (!prev_out || !opt_seq_lens || !block_table || !seq_lens || !bonus)
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "a request input/output pointer is NULL");
+  if (n_rows > 0 && (!row_req || !opt_positions || !positions || !slot_mapping))
+    return fail(DFLASH_ERR_INVALID_ARGUMENT, "a row input/output pointer is NULL");
+  PrepareArgs a{};
+  a.B = batch;
+  a.K = prev_num_drafts;
+  a.V = vocab;
+  a.n_rows = n_rows;
+  a.maxb = max_blocks_per_seq;
+  a.P = page_size;
+  a.prev_out = prev_out;
+  a.opt_seq_lens = opt_seq_lens;
+  a.row_req = row_req;
+  a.opt_positions = opt_positions;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.positions = positions;
+  a.bonus = bonus;
+  a.slot_mapping = slot_mapping;
+  HIP_TRY(launch_prepare(a, (hipStream_t)stream));
   return ok();
 }
 

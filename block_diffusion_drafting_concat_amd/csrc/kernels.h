@@ -117,8 +117,17 @@ hipError_t launch_argmax_reduce(int B, int K, int ngroups, const float *val, con
                                 const int32_t *bonus, int V, int32_t *draft_ids, int32_t *drafts_only,
                                 hipStream_t s);
 
+// stats (optional, [3] int64): += B, B*K, sum(acc - 1)
 hipError_t launch_verify(int B, int K, const int32_t *drafts, const int32_t *target, int32_t *acc, int32_t *out,
-                         int32_t *next_bonus, hipStream_t s);
+                         int32_t *next_bonus, int64_t *stats, hipStream_t s);
+
+struct PrepareArgs {
+  int B, K, V, n_rows, maxb, P;
+  const int32_t *prev_out, *opt_seq_lens, *row_req, *opt_positions, *block_table;
+  int32_t *seq_lens, *positions, *bonus;
+  int64_t *slot_mapping;
+};
+hipError_t launch_prepare(const PrepareArgs &a, hipStream_t s);
 
 hipError_t launch_rope_table(int D, double theta, int max_pos, float *cos_out, float *sin_out, hipStream_t s);
 

@@ -1,5 +1,5 @@
 // Row-wise kernels of the DFlash path: block embedding, the LM-head argmax reduction, greedy
-// verification and the RoPE table. Normalisation, q/k norm + RoPE, SwiGLU and the context
+// verification (with acceptance counters), proposal-input preparation and the RoPE table. Normalisation, q/k norm + RoPE, SwiGLU and the context
 // K/V scatter run as GEMM epilogues or prologues.
 #include <float.h>
 
@@ -86,11 +86,16 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(int B, int K, int ng
 
 // ---------------------------------------------------------------------------------------
 // Greedy verification: one wave per sequence; lane i compares draft i with target i and the
-// first mismatch (lowest set bit of the ballot) ends the accepted prefix.
+// first mismatch (lowest set bit of the ballot) ends the accepted prefix. With stats, the
+// acceptance counters are accumulated with integer atomics (order-independent).
 __global__ void verify_kernel(int B, int K, const int32_t *drafts, const int32_t *target, int32_t *acc,
-                              int32_t *out, int32_t *next_bonus) {
+                              int32_t *out, int32_t *next_bonus, int64_t *stats) {
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (stats && blockIdx.x == 0 && threadIdx.x == 0) {
+    atomicAdd(reinterpret_cast<unsigned long long *>(&stats[0]), (unsigned long long)B);
+    atomicAdd(reinterpret_cast<unsigned long long *>(&stats[1]), (unsigned long long)B * K);
+  }
   if (b >= B) return;
   const bool mismatch = lane < K && drafts[(size_t)b * K + lane] != target[(size_t)b * (K + 1) + lane];
   const unsigned long long mask = __ballot(mismatch);
@@ -100,6 +105,42 @@ __global__ void verify_kernel(int B, int K, const int32_t *drafts, const int32_t
   if (lane == 0) {
     acc[b] = a;
     next_bonus[b] = target[(size_t)b * (K + 1) + n];
+    if (stats && n > 0) atomicAdd(reinterpret_cast<unsigned long long *>(&stats[2]), (unsigned long long)n);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Proposal-input preparation: threads [0, B) correct the requests (sequence length, bonus),
+// threads [B, B + n_rows) the context rows (position, slot); each counts the valid entries of
+// its request's previous output itself (K + 1 <= 64 reads).
+__global__ void prepare_kernel(PrepareArgs a) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.B + a.n_rows) return;
+  const bool is_req = t < a.B;
+  const int r = t - a.B;
+  const int b = is_req ? t : min(max(a.row_req[r], 0), a.B - 1);
+  const int32_t *prev = a.prev_out + (size_t)b * (a.K + 1);
+  int valid = 0, last = -1;
+  for (int i = 0; i <= a.K; ++i) {
+    const int v = prev[i];
+    if (v != -1 && v >= 0 && v < a.V) {
+      ++valid;
+      last = v;
+    }
+  }
+  const int rejected = a.K + 1 - valid;
+  if (is_req) {
+    a.seq_lens[b] = a.opt_seq_lens[b] - rejected;
+    a.bonus[b] = last >= 0 ? last : 0;
+  } else {
+    const int pos = a.opt_positions[r] - rejected;
+    a.positions[r] = pos;
+    int64_t slot = -1;
+    if (pos >= 0) {
+      const int page = a.block_table[(size_t)b * a.maxb + min(pos / a.P, a.maxb - 1)];
+      slot = (int64_t)page * a.P + pos % a.P;
+    }
+    a.slot_mapping[r] = slot;
   }
 }
 
@@ -147,9 +188,16 @@ hipError_t launch_argmax_reduce(int B, int K, int ngroups, const float *val, con
 }
 
 hipError_t launch_verify(int B, int K, const int32_t *drafts, const int32_t *target, int32_t *acc, int32_t *out,
-                         int32_t *next_bonus, hipStream_t s) {
+                         int32_t *next_bonus, int64_t *stats, hipStream_t s) {
   ProfScope prof("verify", s);
-  verify_kernel<<<(B + 3) / 4, 256, 0, s>>>(B, K, drafts, target, acc, out, next_bonus);
+  verify_kernel<<<(B + 3) / 4, 256, 0, s>>>(B, K, drafts, target, acc, out, next_bonus, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare(const PrepareArgs &a, hipStream_t s) {
+  ProfScope prof("prepare", s);
+  const int n = a.B + a.n_rows;
+  prepare_kernel<<<(n + 255) / 256, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -183,6 +183,43 @@ dflash_status dflash_greedy_verify(int32_t batch, int32_t num_drafts,
                                    int32_t *accepted_len, int32_t *output_tokens,
                                    int32_t *next_bonus, void *stream);
 
+/* Greedy verification with the acceptance counters of [V]'s spec-decode metrics fused in:
+ * the same outputs as dflash_greedy_verify, and the int64 device array stats[3] is
+ * incremented by this call's num_drafts (batch: one draft block per sequence),
+ * num_draft_tokens (batch * num_drafts) and num_accepted_tokens (sum of accepted_len - 1).
+ * The caller zeroes stats once; acceptance rate = stats[2] / stats[1] and acceptance length
+ * = 1 + stats[2] / stats[0]. Increments are integer atomics, so the totals do not depend on
+ * scheduling. stats must not be NULL. */
+dflash_status dflash_greedy_verify_stats(int32_t batch, int32_t num_drafts,
+                                         const int32_t *draft_tokens, const int32_t *target_tokens,
+                                         int32_t *accepted_len, int32_t *output_tokens,
+                                         int32_t *next_bonus, int64_t *stats, void *stream);
+
+/* Proposal-input preparation ([N] "Async Rejection and Position Correction", "Paged KV
+ * Integration", "Draft Block Construction"): corrects a step that was scheduled as if every
+ * draft of the previous step had been accepted. For request b, prev_out[b] is the previous
+ * step's rejection-sampler output [prev_num_drafts + 1] (emitted tokens, -1 for rejected):
+ *   valid_b = entries that are not -1 and lie in [0, vocab); rejected_b = prev_num_drafts + 1
+ *   - valid_b;
+ *   seq_lens[b] = opt_seq_lens[b] - rejected_b (post-verification length);
+ *   positions[r] = opt_positions[r] - rejected_{row_req[r]} for the n_rows context rows;
+ *   slot_mapping[r] = block_table[req][min(pos / page_size, max_blocks_per_seq - 1)] *
+ *     page_size + pos % page_size, or -1 when the corrected position is negative (injection
+ *     skips it);
+ *   bonus[b] = the last valid entry of prev_out[b] (0 if none), the block's slot-0 token.
+ * row_req values are clamped to [0, batch). Shapes: prev_out [batch, prev_num_drafts + 1];
+ * opt_seq_lens, seq_lens, bonus [batch]; row_req, opt_positions, positions [n_rows] int32;
+ * slot_mapping [n_rows] int64; block_table [batch, max_blocks_per_seq] int32. All device
+ * arrays. Requires 0 <= prev_num_drafts <= 63, page_size > 0, max_blocks_per_seq > 0. */
+dflash_status dflash_prepare_proposal_inputs(int32_t batch, int32_t prev_num_drafts,
+                                             const int32_t *prev_out, int32_t vocab,
+                                             const int32_t *opt_seq_lens, int32_t n_rows,
+                                             const int32_t *row_req, const int32_t *opt_positions,
+                                             const int32_t *block_table,
+                                             int32_t max_blocks_per_seq, int32_t page_size,
+                                             int32_t *seq_lens, int32_t *positions,
+                                             int64_t *slot_mapping, int32_t *bonus, void *stream);
+
 /* Per-kernel timing, for measurement tools. While enabled, every kernel the library launches
  * is bracketed by two hipEvents recorded on the launch's stream. dflash_profile_collect
  * waits for the recorded events and adds each launch's duration to the totals of its kernel

@@ -62,6 +62,20 @@ def test_argument_errors_and_empty_calls():
     assert L.dflash_greedy_verify(1, 64, None, None, None, None, None, None) == -2
     assert L.dflash_greedy_verify(1, 7, None, None, None, None, None, None) == -1
     assert L.dflash_build_rope_table(63, 1e6, 10, None, None, None) == -1
+    # verify with counters: stats is required; prepare: argument ranges and empty calls
+    assert L.dflash_greedy_verify_stats(0, 7, None, None, None, None, None, None, None) == 0
+    assert L.dflash_greedy_verify_stats(1, 7, None, None, None, None, None, None, None) == -1
+    assert L.dflash_greedy_verify_stats(1, 64, None, None, None, None, None, None, None) == -1
+    assert L.dflash_prepare_proposal_inputs(0, 3, None, 10, None, 0, None, None, None, 4, 16, None, None, None,
+                                            None, None) == 0
+    assert L.dflash_prepare_proposal_inputs(0, 3, None, 10, None, 2, None, None, None, 4, 16, None, None, None,
+                                            None, None) == -1
+    assert L.dflash_prepare_proposal_inputs(1, 64, None, 10, None, 0, None, None, None, 4, 16, None, None, None,
+                                            None, None) == -2
+    assert L.dflash_prepare_proposal_inputs(1, 3, None, 10, None, 0, None, None, None, 4, 0, None, None, None,
+                                            None, None) == -1
+    assert L.dflash_prepare_proposal_inputs(1, 3, None, 10, None, 0, None, None, None, 4, 16, None, None, None,
+                                            None, None) == -1
 
 
 def test_workspace_sizes_grow_with_work_and_are_bounded():

@@ -1,0 +1,85 @@
+"""The whole step (prepare -> inject -> propose -> verify with counters) captured once as a
+hipGraph and replayed: every replay, with eager work of the same library in between, must
+reproduce the eager step bit for bit (drafts, verification, cache rows, counters). The library
+enqueues kernels only (no allocation, memset or host synchronisation), which is what makes the
+step capturable."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_drafting_concat_amd import binding, synth
+from tests.gpu_helpers import Setup, gpu_cache_rows
+
+pytestmark = pytest.mark.gpu
+
+SPEC = synth.DrafterSpec(hidden=256, n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=512,
+                         vocab=2048, n_aux=2, target_hidden=192, block_size=16, mask_token_id=2047,
+                         rope_theta=1e6, dtype="bf16")
+
+
+def test_captured_step_replays_match_the_eager_step():
+    ctx = np.array([300, 77, 150], np.int32)
+    st = Setup(SPEC, ctx, seed=3)
+    B, K, n = st.B, SPEC.block_size - 1, 8
+    rng = np.random.default_rng(3)
+    # previous verification output: a_b emitted tokens, then -1
+    prev = rng.integers(0, SPEC.vocab, size=(B, K + 1)).astype(np.int32)
+    a = np.array([1, K + 1, 6])
+    for b in range(B):
+        prev[b, a[b]:] = -1
+    rejected = K + 1 - a
+    row_req = np.repeat(np.arange(B), n).astype(np.int32)
+    true_pos = np.concatenate([np.arange(c - n, c) for c in ctx]).astype(np.int32)
+    aux = [synth.aux_states(SPEC, st.seed, b, int(ctx[b]) - n, n) for b in range(B)]
+    aux_d = [torch.cat([x[j] for x in aux]).cuda() for j in range(SPEC.n_aux)]
+    cu = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    prev_d, req_d, bt_d = cu(prev), cu(row_req), cu(st.bt)
+    opt_seq_d, opt_pos_d = cu((ctx + rejected).astype(np.int32)), cu((true_pos + rejected[row_req]).astype(np.int32))
+    target = cu(rng.integers(0, SPEC.vocab, size=(B, K + 1)).astype(np.int32))
+    prep = (torch.empty(B, dtype=torch.int32, device="cuda"), torch.empty(B * n, dtype=torch.int32, device="cuda"),
+            torch.empty(B * n, dtype=torch.int64, device="cuda"), torch.empty(B, dtype=torch.int32, device="cuda"))
+    out = (torch.empty((B, K + 1), dtype=torch.int32, device="cuda"),
+           torch.empty((B, K), dtype=torch.int32, device="cuda"))
+    vout = (torch.empty(B, dtype=torch.int32, device="cuda"), torch.empty((B, K + 1), dtype=torch.int32, device="cuda"),
+            torch.empty(B, dtype=torch.int32, device="cuda"))
+    stats = torch.zeros(3, dtype=torch.int64, device="cuda")
+    ws_inj = st.dev.workspace(binding.DFLASH_OP_INJECT, B * n)
+
+    def step():
+        seq, pos, slots, bonus = binding.prepare(prev_d, SPEC.vocab, opt_seq_d, req_d, opt_pos_d, bt_d, st.P, out=prep)
+        st.dev.inject(st.cache, aux_d, pos, slots, ws_inj)
+        st.dev.propose(st.cache, bonus, seq, st.max_ctx, st.ws_prop, out=out)
+        binding.verify_with_stats(out[1], target, stats, out=vout)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (*prep, *out, *vout)]
+    ref_rows = [gpu_cache_rows(st, b, np.arange(int(ctx[b]) - n, int(ctx[b]))) for b in range(B)]
+    assert np.array_equal(prep[0].cpu().numpy(), ctx) and np.array_equal(prep[1].cpu().numpy(), true_pos)
+    per_step = stats.clone()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    stats.zero_()
+    other = (torch.empty((B, K + 1), dtype=torch.int32, device="cuda"),
+             torch.empty((B, K), dtype=torch.int32, device="cuda"))
+    for replay in range(4):
+        for t in (*prep, *out, *vout):
+            t.fill_(-7)
+        for l in range(SPEC.n_layers):  # the replay must rewrite the injected rows
+            for t in (st.cache.k[l], st.cache.v[l]):
+                t.view(-1, SPEC.n_kv_heads, SPEC.head_dim)[prep[2].new_tensor(
+                    st.slots(0, np.arange(int(ctx[0]) - n, int(ctx[0])))).long()] = 0
+        graph.replay()
+        # eager work of the same library between replays
+        st.dev.propose(st.cache, cu(np.full(B, 5, np.int32)), cu(ctx), st.max_ctx, st.ws_prop, out=other)
+        torch.cuda.synchronize()
+        for got, want in zip((*prep, *out, *vout), ref):
+            assert torch.equal(got, want), replay
+        for b in range(B):
+            rows = gpu_cache_rows(st, b, np.arange(int(ctx[b]) - n, int(ctx[b])))
+            for g_l, w_l in zip(rows[0] + rows[1], ref_rows[b][0] + ref_rows[b][1]):
+                assert np.array_equal(g_l, w_l), (replay, b)
+    assert torch.equal(stats, 4 * per_step)
