@@ -70,18 +70,34 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const T *vbk = reinterpret_cast<const T *>(a.vb);
   const int32_t *bt = a.block_table + (size_t)b * a.maxb;
 
+  // The page of each key this thread stages, read for a whole tile ahead: the page-table
+  // reads depend only on the key index (clamped into the table), not on the context length,
+  // so the first tile's go out together with the length and the queries.
+  constexpr int kVecPerThread = kTileKeys * CPR / 256;
+  static_assert(kTileKeys * CPR % 256 == 0, "staging vectors per thread");
+  int pages[kVecPerThread];
+  auto load_pages = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      const int t = t0 + ((int)threadIdx.x + i * 256) / CPR;
+      pages[i] = bt[min(t / a.P, a.maxb - 1)];
+    }
+  };
+  load_pages(kbeg);
+
   for (int t0 = kbeg; t0 < kend; t0 += kTileKeys) {
     // ---- stage the K tile (row-major) and V tile (transposed) in LDS
     __syncthreads();
-    for (int v = threadIdx.x; v < kTileKeys * CPR; v += 256) {
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      const int v = threadIdx.x + i * 256;
       const int key = v / CPR, part = v % CPR;
       const int t = t0 + key;
       Vec16 kv = zero_vec16(), vv = zero_vec16();
       if (t < kend) {
         const T *ksrc, *vsrc;
         if (t < c) {
-          int page = bt[min(t / a.P, a.maxb - 1)];
-          page = min(max(page, 0), a.num_pages - 1);
+          const int page = min(max(pages[i], 0), a.num_pages - 1);
           const size_t off = ((size_t)(page * a.P + t % a.P) * a.KVH + g) * D + part * KPV;
           ksrc = kc + off;
           vsrc = vc + off;
@@ -99,6 +115,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < KPV; ++e) vts[(part * KPV + e) * VSTR + key] = ve[e];
     }
+    if (t0 + kTileKeys < kend) load_pages(t0 + kTileKeys);  // in flight during this tile
     __syncthreads();
     if (wave * 16 >= R) continue;
 
@@ -185,11 +202,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   l_run += __shfl_xor(l_run, 32, 64);
   const size_t base = ((size_t)(b * a.KVH + g) * a.nsplit + split) * 64;
   if (rvalid) {
-    float *po = a.po + (base + r) * D;
+    float *po = a.po + (base + r) * D + (lane >> 4) * 4;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) po[db * 16 + (lane >> 4) * 4 + i] = acc_o[db][i];
+    for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4_t *>(po + db * 16) = acc_o[db];
     if (lane < 16) {
       a.pm[base + r] = m_run;
       a.pl[base + r] = l_run;
@@ -197,49 +212,56 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split partials of one (sequence, kv head, query row); one thread per element of
-// the head vector. The split weights exp2(m_s - max m) are computed once into LDS.
+// Merge the split partials of one (sequence, kv head, query row). Thread (d, sub) sums the
+// splits s = sub (mod 256 / D) for element d with the split weights exp2(m_s - max m); the
+// loads of 16 splits are issued together, and the sub-sums are combined through LDS in a
+// fixed order.
 template <typename T>
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
-  extern __shared__ float wsplit[];  // [nsplit]
-  __shared__ float red[16];
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  __shared__ float red[4];
+  __shared__ float rnum[256];
+  __shared__ float rden[4];
   const int row = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.QH / a.KVH;
-  const int D = a.D;
+  const int D = a.D, nsub = 256 / D;
+  const int d = threadIdx.x % D, sub = threadIdx.x / D;
   const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
-  const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64;
+  const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64 + row;
   float mloc = -INFINITY;
-  for (int s = threadIdx.x; s < ns; s += blockDim.x) mloc = fmaxf(mloc, a.pm[base + s * 64 + row]);
+  for (int s = threadIdx.x; s < ns; s += 256) mloc = fmaxf(mloc, a.pm[base + (size_t)s * 64]);
   mloc = wave_max(mloc);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mloc;
   __syncthreads();
-  float mmax = red[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) mmax = fmaxf(mmax, red[i]);
-  __syncthreads();
-  float dloc = 0.f;
-  for (int s = threadIdx.x; s < ns; s += blockDim.x) {
-    const float wgt = exp2f(a.pm[base + s * 64 + row] - mmax);
-    wsplit[s] = wgt;
-    dloc += wgt * a.pl[base + s * 64 + row];
-  }
-  const float den = block_sum(dloc, red);  // synchronises, so wsplit is visible
-  const int hh = row / a.bs, j = row % a.bs;
-  float *o = a.o + ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    const float *po = a.po + (base + row) * D + d;
-    float num = 0.f;
-    int s = 0;
-    for (; s + 4 <= ns; s += 4) {
-      const float p0 = po[(size_t)(s + 0) * 64 * D], p1 = po[(size_t)(s + 1) * 64 * D];
-      const float p2 = po[(size_t)(s + 2) * 64 * D], p3 = po[(size_t)(s + 3) * 64 * D];
-      num += wsplit[s] * p0;
-      num += wsplit[s + 1] * p1;
-      num += wsplit[s + 2] * p2;
-      num += wsplit[s + 3] * p3;
+  const float mmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float num = 0.f, den = 0.f;
+  for (int s0 = sub; s0 < ns; s0 += 16 * nsub) {
+    float pv[16], mv[16], lv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int s = min(s0 + u * nsub, ns - 1);
+      pv[u] = a.po[(base + (size_t)s * 64) * D + d];
+      mv[u] = a.pm[base + (size_t)s * 64];
+      lv[u] = a.pl[base + (size_t)s * 64];
     }
-    for (; s < ns; ++s) num += wsplit[s] * po[(size_t)s * 64 * D];
-    o[d] = num / den;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float w = s0 + u * nsub < ns ? exp2f(mv[u] - mmax) : 0.f;
+      num += w * pv[u];
+      den += w * lv[u];
+    }
+  }
+  rnum[threadIdx.x] = num;
+  if (d == 0) rden[sub] = den;
+  __syncthreads();
+  if (sub == 0) {
+    float n = 0.f, dn = 0.f;
+    for (int q = 0; q < nsub; ++q) {
+      n += rnum[q * D + d];
+      dn += rden[q];
+    }
+    const int hh = row / a.bs, j = row % a.bs;
+    a.o[((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d] = n / dn;
   }
 }
 
@@ -258,7 +280,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
   const int G = a.QH / a.KVH;
   {
     ProfScope prof("attn_merge", s);
-    attn_merge_kernel<T><<<dim3(a.bs * G, a.KVH, a.B), a.D, a.nsplit * sizeof(float), s>>>(a);
+    attn_merge_kernel<T><<<dim3(a.bs * G, a.KVH, a.B), 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -10,12 +10,15 @@
 //    v_mfma_f32_16x16x32_bf16 directly (B operand = 16 W rows x 64 contiguous bytes), in
 //    ping-pong register buffers so that two groups of loads are in flight; one A fragment
 //    read from LDS serves all CT tiles;
-//  * the activation slice is staged in LDS in passes (up to ~150 KiB when the work-group
-//    has the CU to itself), so the vector-memory path carries only weights. fp32
-//    activations are staged as an exact pair of bf16 planes (hi, lo) and cost two MFMAs per
-//    step. RMSNorm can be applied while staging ("norm on load"): row scales come from
-//    per-column-group sums of squares written by the producer of the rows, the norm weight
-//    from its vector;
+//  * the activation slice is staged in LDS in passes (up to ~132 KiB when the work-group
+//    has the CU to itself), so the MFMA loop reads only weights from memory. fp32
+//    activations (one row tile) are moved by LDS DMA: every wave issues global->LDS loads
+//    of 1 KiB segments that need no registers, so a whole pass is in flight at once while
+//    the first weight groups load; the pass is then converted in place to an exact pair of
+//    bf16 values (hi, lo) per element, which costs two MFMAs per step. RMSNorm can be
+//    applied while converting ("norm on load"): row scales come from per-column-group sums
+//    of squares written by the producer of the rows, the norm weight slice arrives by DMA
+//    with the pass;
 //  * a work-group may own several column groups (up to NCG): K passes are then the outer
 //    loop, so each staged pass serves all of them and the accumulators stay in registers;
 //  * the KW sub-slice tiles are summed through LDS in a fixed order into the work-group's
@@ -38,6 +41,22 @@ constexpr int kDefaultPassBytes = 60 << 10;  // LDS for one staged A pass unless
 constexpr int kMaxLds = 160 << 10;           // LDS of one CU
 constexpr int kStageVecs = 2;                // A vectors staged per thread per round
 constexpr int kMaxGroupsPerWg = 8;           // column groups of one persistent work-group, max
+#ifndef DFLASH_DMA_STAGING
+#define DFLASH_DMA_STAGING 1
+#endif
+constexpr bool kDmaStaging = DFLASH_DMA_STAGING != 0;  // fp32 activations staged by LDS DMA
+
+// LDS of one staged pass of fp32 activations (DMA staging): rows of whole 1 KiB DMA
+// segments plus 16 bytes of padding (the 16 rows of an MFMA fragment read then fall on
+// distinct banks), followed by the pass's slice of the norm weight.
+__host__ __device__ constexpr int dma_row_bytes(int kp) { return (kp * 4 + 1023) / 1024 * 1024 + 16; }
+__host__ __device__ constexpr int dma_w_bytes(int kp) { return (kp * 2 + 1023) / 1024 * 1024; }
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane (lds must be
+// uniform across the wave).
+__device__ __forceinline__ void dma16(const void *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
 
 template <typename T>
 __host__ __device__ constexpr int ch_of() {
@@ -45,8 +64,12 @@ __host__ __device__ constexpr int ch_of() {
 }
 
 // K steps per register buffer: about 8 16-byte weight loads per lane in each of the two
-// buffers.
-__host__ __device__ constexpr int group_steps(int ct, int nacc) { return ct * nacc >= 8 ? 1 : 8 / (ct * nacc); }
+// buffers, 4 when the work-group splits K among its waves (those run several work-groups to
+// a CU). Loads in flight beyond what covers the memory latency only lengthen the queues: every
+// dependent access of the kernel (activation staging, the split-K hand-off) then waits longer.
+__host__ __device__ constexpr int group_steps(int ct, int nacc, int kw) {
+  return ct * nacc >= (kw > 1 ? 4 : 8) ? 1 : (kw > 1 ? 4 : 8) / (ct * nacc);
+}
 
 // Per-head RMSNorm + rotate-half RoPE of one head vector held by one wave: lane i < D/2 owns
 // the pair (i, i + D/2).
@@ -69,16 +92,23 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
   constexpr int CH = ch_of<T>();
   constexpr bool kDual = E == GemmEpi::kSwiGLU;
   constexpr int NACC = kDual ? 2 : 1;
-  constexpr int U = group_steps(CT, NACC);
+  constexpr int U = group_steps(CT, NACC, KW);
   constexpr int NPL = kAF32 ? 2 : 1;                 // A planes in LDS
   constexpr bool kF32Src = kAF32 || sizeof(T) == 4;  // A source is fp32
   constexpr int NSRC = kAF32 ? 2 : 1;                // 16-byte source loads per staged vector
   constexpr int TR = 16 * MT, TC = 16 * CW * CT;     // final tile rows, columns
+  constexpr bool kDma = kAF32 && kDmaStaging && MT == 1;
   static_assert(!kAF32 || (KPV == 8 && !kMultiA), "fp32 activations pair with bf16 weights");
-  // LDS: [A pass: NPL planes of TR x (kp + KPV)] [red: NW*NACC*CT*256][fin: NACC*TR*TC]
+  // LDS: [A pass][red: NW*NACC*CT*256][fin: NACC*TR*TC]. The A pass is NPL planes of
+  // TR x (kp + KPV) elements, or with DMA staging TR rows of dma_row_bytes(kp) then the norm
+  // weight slice: each row is first the raw fp32 values, then converted in place to 32-byte
+  // chunks [8 bf16 hi][8 bf16 lo] of 8 consecutive columns.
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T *sa = reinterpret_cast<T *>(smem);
-  float *red = reinterpret_cast<float *>(smem + (size_t)NPL * TR * (g.kp + KPV) * sizeof(T));
+  const int rs = dma_row_bytes(g.kp);  // DMA staging: LDS bytes per A row
+  unsigned char *sw = smem + (size_t)TR * rs;
+  float *red = reinterpret_cast<float *>(
+      smem + (kDma ? (size_t)TR * rs + dma_w_bytes(g.kp) : (size_t)NPL * TR * (g.kp + KPV) * sizeof(T)));
   float *fin = red + NW * NACC * CT * 256;
   __shared__ float s_inv[TR];  // norm on load: per-row 1/rms
   __shared__ unsigned s_flag;
@@ -101,6 +131,57 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
   auto src_row = [&](int m) {
     return g.keep_bs > 0 ? (m / (g.keep_bs - 1)) * g.keep_bs + m % (g.keep_bs - 1) + 1 : m;
   };
+  // DMA staging: every wave issues global->LDS loads of 1 KiB segments (a lane moves 16
+  // bytes; the LDS address is uniform per instruction), so the whole pass is in flight at
+  // once without registers. Columns past the pass read a clamped valid address; they are
+  // never used.
+  auto issue_dma = [&](int p0, int plen) {
+    const int segs = (plen * 4 + 1023) / 1024;
+    const float *a0 = reinterpret_cast<const float *>(g.a[0]);
+    for (int q = wave; q < TR * segs; q += NW) {
+      const int r = q / segs, sg = q % segs;
+      const int m = src_row(min(m0 + r, g.M - 1));
+      const int c = min(sg * 256 + lane * 4, plen - 4);
+      dma16(a0 + (size_t)m * g.lda + p0 + c, smem + (size_t)r * rs + sg * 1024);
+    }
+    if (norm) {
+      const T *w0 = reinterpret_cast<const T *>(g.norm_w);
+      for (int q = wave; q * 512 < plen; q += NW)
+        dma16(w0 + p0 + min(q * 512 + lane * 8, plen - 8), sw + q * 1024);
+    }
+  };
+  // W row of this lane in each of the wave's column tiles of column group cg (a column past N
+  // reads a valid row of the first segment; its results are never stored)
+  auto set_rows = [&](const T *(&brow)[NACC][CT], int cg) {
+    const int nw0 = cg * TC + cw * CT * 16;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int ncol = nw0 + c * 16;
+      int seg = 0, nbase = 0;
+      if (!kDual)
+        while (seg < g.b_nseg - 1 && ncol >= g.b_end[seg]) nbase = g.b_end[seg++];
+      const bool act = ncol < g.N;
+      const int r = (act ? ncol - nbase : 0) + (lane & 15);
+      brow[0][c] = reinterpret_cast<const T *>(g.b[act ? seg : 0]) + (size_t)r * g.K + kg;
+      if (kDual) brow[NACC - 1][c] = reinterpret_cast<const T *>(g.b[1]) + (size_t)r * g.K + kg;
+    }
+  };
+
+  // The first pass's activations (DMA) and first weight group go out before anything waits:
+  // the row scales' loads then overlap them.
+  if constexpr (kDma) issue_dma(kb, min(g.kp, ke - kb));
+  Vec16 b0[NACC][CT][U], b1[NACC][CT][U];
+  {
+    const int plen = min(kp, ke - kb), q0 = kw * kq;
+    const T *brow[NACC][CT];
+    set_rows(brow, blockIdx.x);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) b0[a][c][u] = load_vec16(brow[a][c] + kb + min(q0 + u * CH, plen - CH));
+  }
   if (norm) {
     // TPR threads per row sum the row's per-column-group sums of squares (fixed order)
     constexpr int TPR0 = NT / TR;
@@ -187,6 +268,40 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
     }
   };
 
+  // DMA staging: wait for the pass, then convert it in place (norm on load, rows past M
+  // zeroed, hi/lo split); the normalised rows also go to a_out from the first column group.
+  auto convert_dma = [&](int p0, int plen, bool write_out) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA has landed
+    __syncthreads();
+    const int nch = plen / 8;
+    for (int v = threadIdx.x; v < TR * nch; v += NT) {
+      const int r = v / nch, c = v % nch;
+      unsigned char *pc = smem + (size_t)r * rs + c * 32;
+      float f[8];
+      __builtin_memcpy(f, pc, 32);
+      if (norm) {
+        T wv[8];
+        __builtin_memcpy(wv, sw + c * 16, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = f[e] * s_inv[r] * Storage<T>::load(wv, e);
+      }
+      const bool ok = m0 + r < g.M;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = ok ? f[e] : 0.f;
+      if (write_out && ok)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) g.a_out[(size_t)(m0 + r) * g.K + p0 + c * 8 + e] = f[e];
+      uint16_t hl[16];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hl[e] = f32_to_bf16(f[e]);
+        hl[8 + e] = f32_to_bf16(f[e] - bf16_to_f32(hl[e]));
+      }
+      __builtin_memcpy(pc, hl, 32);
+    }
+    __syncthreads();
+  };
+
   // The work-group's column groups: cg_i = blockIdx.x + i * gridDim.x for i < NCG (cg_i < ncg),
   // one accumulator set each. K passes are the outer loop, so each pass of A is staged once
   // and serves every column group of the work-group.
@@ -199,23 +314,6 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
       for (int c = 0; c < CT; ++c)
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[i][a][c][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // W row of this lane in each of the wave's column tiles of column group cg (a column past N
-  // reads a valid row of the first segment; its results are never stored)
-  auto set_rows = [&](const T *(&brow)[NACC][CT], int cg) {
-    const int nw0 = cg * TC + cw * CT * 16;
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      const int ncol = nw0 + c * 16;
-      int seg = 0, nbase = 0;
-      if (!kDual)
-        while (seg < g.b_nseg - 1 && ncol >= g.b_end[seg]) nbase = g.b_end[seg++];
-      const bool act = ncol < g.N;
-      const int r = (act ? ncol - nbase : 0) + (lane & 15);
-      brow[0][c] = reinterpret_cast<const T *>(g.b[act ? seg : 0]) + (size_t)r * g.K + kg;
-      if (kDual) brow[NACC - 1][c] = reinterpret_cast<const T *>(g.b[1]) + (size_t)r * g.K + kg;
-    }
-  };
 
   for (int p0 = kb; p0 < ke; p0 += kp) {
     const int plen = min(kp, ke - p0);  // a multiple of CH
@@ -244,14 +342,15 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           const int ao = (t * 16 + (lane & 15)) * as + k + kg;
+          const unsigned char *pd = smem + (size_t)(t * 16 + (lane & 15)) * rs + ((k + kg) >> 3) * 32;
           Vec16 af;
-          af.u = *reinterpret_cast<const uint4 *>(sa + ao);
+          af.u = kDma ? *reinterpret_cast<const uint4 *>(pd) : *reinterpret_cast<const uint4 *>(sa + ao);
 #pragma unroll
           for (int c = 0; c < CT; ++c)
 #pragma unroll
             for (int a = 0; a < NACC; ++a) mma16<T>(acc[i][a][c][t], af, bf[a][c]);
           if constexpr (kAF32) {
-            af.u = *reinterpret_cast<const uint4 *>(sa_lo + ao);
+            af.u = kDma ? *reinterpret_cast<const uint4 *>(pd + 16) : *reinterpret_cast<const uint4 *>(sa_lo + ao);
 #pragma unroll
             for (int c = 0; c < CT; ++c)
 #pragma unroll
@@ -274,9 +373,16 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
       // Loads are issued unconditionally (addresses clamped into the operand) so that the
       // compiler counts outstanding loads exactly: weight loads stay in flight across the A
       // staging and across each MFMA group.
-      Vec16 b0[NACC][CT][U], b1[NACC][CT][U];
-      load_group(b0, 0);
-      if (i == 0) {
+      if (p0 != kb || i != 0) load_group(b0, 0);  // the first one was issued at the start
+      if (kDma && i == 0) {
+        // ---- A rows [m0, m0 + TR) x K [p0, p0 + plen) into LDS by DMA (the first pass was
+        //      issued at the start; a later one once every wave is done with the previous)
+        if (p0 != kb) {
+          __syncthreads();
+          issue_dma(p0, plen);
+        }
+        convert_dma(p0, plen, g.a_out != nullptr && blockIdx.x == 0);
+      } else if (i == 0) {
         // ---- A rows [m0, m0 + TR) x K [p0, p0 + plen) into LDS; the first round's loads
         //      and the first weight group are in flight together
         const int total = TR * vrow;
@@ -322,6 +428,15 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
     const int cg = blockIdx.x + i * gridDim.x;
     if (cg >= ncg) break;
     const int n0 = cg * TC;
+    // residual-add: the tile's residual values load now, so the hand-off below hides them
+    constexpr int NRES = E == GemmEpi::kResidAdd ? (TR * TC + NT - 1) / NT : 1;
+    float res[NRES];
+#pragma unroll
+    for (int j = 0; j < NRES; ++j) {
+      const int e = threadIdx.x + j * NT;
+      const int m = m0 + e / TC, n = n0 + e % TC;
+      res[j] = E == GemmEpi::kResidAdd && e < TR * TC && m < g.M && n < g.N ? g.out[(size_t)m * g.N + n] : 0.f;
+    }
 
     // ---- KW sub-slice tiles -> the work-group's tile fin[a][row][col], summed in fixed order.
     //      MFMA tile layout: lane holds rows (lane/16)*4 + i, column lane%16 at [lane*4 + i].
@@ -395,14 +510,16 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
 
     // ---- epilogues on the final tile
     if constexpr (E == GemmEpi::kStore || E == GemmEpi::kResidAdd) {
-      for (int e = threadIdx.x; e < TR * TC; e += NT) {
+#pragma unroll
+      for (int j = 0; j < (TR * TC + NT - 1) / NT; ++j) {
+        const int e = threadIdx.x + j * NT;
+        if (e >= TR * TC) break;
         const int row = e / TC, col = e % TC;
         const int m = m0 + row, n = n0 + col;
         float v = fin[e];
         if (m < g.M && n < g.N) {
-          const size_t o = (size_t)m * g.N + n;
-          if (E == GemmEpi::kResidAdd) v += g.out[o];
-          g.out[o] = v;
+          if constexpr (E == GemmEpi::kResidAdd) v += res[j];
+          g.out[(size_t)m * g.N + n] = v;
         } else {
           v = 0.f;
         }
@@ -506,7 +623,8 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
 template <typename T, int MT, int CW, int CT, int KW, GemmEpi E, bool kAF32>
 size_t lds_bytes(const GemmArgs &g) {
   constexpr int KPV = Storage<T>::kPerVec;
-  const size_t a = (size_t)16 * MT * (g.kp + KPV) * sizeof(T) * (kAF32 ? 2 : 1);
+  const size_t a = kAF32 && kDmaStaging && MT == 1 ? (size_t)16 * dma_row_bytes(g.kp) + dma_w_bytes(g.kp)
+                                        : (size_t)16 * MT * (g.kp + KPV) * sizeof(T) * (kAF32 ? 2 : 1);
   const int nacc = E == GemmEpi::kSwiGLU ? 2 : 1;
   const size_t r = ((size_t)CW * KW * nacc * CT * 256 + (size_t)nacc * 16 * MT * 16 * CW * CT) * sizeof(float);
   return a + r;
@@ -599,12 +717,11 @@ int cu_count() {
 }  // namespace
 
 // Work-group shape, K splits and column groups per work-group. At most 16 activation rows
-// (one MFMA row tile) the GEMM is a pure weight stream with one work-group per CU (register
-// and LDS use keep it at one):
+// (one MFMA row tile) the GEMM is a pure weight stream:
 //  * more column groups than CUs (the LM head): each work-group owns up to
 //    kMaxGroupsPerWg column groups, stages each K pass of the activations once (passes of up
-//    to 128 KiB) and streams all its column groups per pass;
-//  * fewer: split-K until there are about as many work-groups as CUs.
+//    to ~132 KiB) and streams all its column groups per pass;
+//  * fewer: split-K until there are about two work-groups per CU.
 // The shapes were chosen by timing every instantiated shape and split count on the
 // Qwen3-8B-shaped projections: 8 wave columns for the LM head and the long-K projections (the
 // down projection, fc over the concatenated target states), 4-wave work-groups (several per
@@ -639,12 +756,16 @@ GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bo
     const int per = (p.col_groups + cus - 1) / cus;
     if (per <= kMaxGroupsPerWg) {
       p.grid_x = (p.col_groups + per - 1) / per;
-      p.lds_budget = 128 << 10;
+      p.lds_budget = 136 << 10;
     }
   }
   const long wgs = (long)(p.grid_x ? p.grid_x : p.col_groups) * p.row_blocks;
-  // 4-wave work-groups (SwiGLU) run three to a CU
-  const long target = mt > 1 ? 4L * cus : (p.cw * p.kw == 4 && epi == GemmEpi::kSwiGLU) ? 3L * cus : cus;
+  // splits toward about two work-groups per CU (three 4-wave SwiGLU ones; one for the
+  // concatenated-input projection, whose activation staging is the longest)
+  const long target = mt > 1                                               ? 4L * cus
+                      : (p.cw * p.kw == 4 && epi == GemmEpi::kSwiGLU) ? 3L * cus
+                      : multi_a                                        ? cus
+                                                                       : 2L * cus;
   int s = 1;
   if (epi != GemmEpi::kArgmax && p.grid_x == 0)
     while (wgs * s * 2 <= target && K % (2 * s * step) == 0 && K / (2 * s) >= 256 && s < 64) s *= 2;
@@ -672,8 +793,12 @@ hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, const GemmPla
   const int budget = p.lds_budget > 0 ? p.lds_budget : kDefaultPassBytes;
   const int kp_max = budget / (16 * mt * esz) / step * step;
   if (kp_max < step) return hipErrorInvalidValue;
-  const int npass = (g.kt + kp_max - 1) / kp_max;
-  g.kp = ((g.kt + npass - 1) / npass + step - 1) / step * step;
+  int npass = (g.kt + kp_max - 1) / kp_max;
+  auto kp_of = [&](int np) { return ((g.kt + np - 1) / np + step - 1) / step * step; };
+  g.kp = kp_of(npass);
+  // DMA staging rounds rows up to whole 1 KiB segments: more passes if that overflows
+  while (af32 && kDmaStaging && mt == 1 && g.kp > step && 16 * dma_row_bytes(g.kp) + dma_w_bytes(g.kp) > budget)
+    g.kp = kp_of(++npass);
   if (!bf16) return launch_dt<float, false>(g, epi, p, s);
   return af32 ? launch_dt<uint16_t, true>(g, epi, p, s) : launch_dt<uint16_t, false>(g, epi, p, s);
 }
