@@ -17,14 +17,16 @@ SPEC = synth.DrafterSpec(hidden=256, n_layers=2, n_q_heads=8, n_kv_heads=2, head
                          rope_theta=1e6, dtype="bf16")
 
 
-def test_captured_step_replays_match_the_eager_step():
-    ctx = np.array([300, 77, 150], np.int32)
+@pytest.mark.parametrize("ctx,acc", [([300, 77, 150], [1, SPEC.block_size, 6]),
+                                     ([300], [6])])  # one sequence: the chained post-attention block
+def test_captured_step_replays_match_the_eager_step(ctx, acc):
+    ctx = np.array(ctx, np.int32)
     st = Setup(SPEC, ctx, seed=3)
     B, K, n = st.B, SPEC.block_size - 1, 8
     rng = np.random.default_rng(3)
     # previous verification output: a_b emitted tokens, then -1
     prev = rng.integers(0, SPEC.vocab, size=(B, K + 1)).astype(np.int32)
-    a = np.array([1, K + 1, 6])
+    a = np.array(acc)
     for b in range(B):
         prev[b, a[b]:] = -1
     rejected = K + 1 - a
