@@ -107,7 +107,7 @@ InjectPlan plan_inject(const dflash_config *c, int rows) {
   const bool bf = is_bf16(c);
   const int H = c->hidden, D = c->head_dim;
   const int kvn = std::max(c->n_layers * 2 * c->n_kv_heads * D, 16);
-  p.fc = gemm_plan(rows, H, c->n_aux * c->target_hidden, D, bf, GemmEpi::kStore, c->n_aux > 1);
+  p.fc = gemm_plan(rows, H, c->n_aux * c->target_hidden, D, bf, GemmEpi::kStore, c->n_aux > 1, false);
   p.kv = gemm_plan(rows, kvn, H, D, bf, GemmEpi::kKvScatter, false);
   p.n_ctr = std::max(gemm_tiles(p.fc), gemm_tiles(p.kv));
   const size_t part = std::max(gemm_part_floats(p.fc, rows, H, GemmEpi::kStore),

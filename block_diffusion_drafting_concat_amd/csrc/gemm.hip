@@ -620,6 +620,231 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
   }  // column groups of this work-group
 }
 
+
+// ---- Many rows (M > 64): LDS-tiled MFMA GEMM. A work-group computes a 128 x 128 tile of
+//      C = A W^T with 4 waves (2 x 2, 64 x 64 each, 4 x 4 MFMA tiles) and walks K in steps of
+//      32, double-buffered: the weight tile goes global -> LDS by DMA, the fp32 activation tile
+//      through registers, where it is normalised (norm on load) and split into the exact (hi,
+//      lo) bf16 pair; one step's loads are in flight while the previous step's 32 MFMAs per wave
+//      run. Both LDS tiles are [128 rows][32] bf16 with the 16-byte chunks of a row XOR-swizzled
+//      by (row / 4) % 4, so the 16 rows of a fragment read fall on distinct banks. The tile then
+//      goes through LDS to the epilogue (fp32 store / residual add with per-tile row sums of
+//      squares, SwiGLU, per-tile argmax). Work-group order puts every row tile of a column tile
+//      on one XCD, back to back, so the weight tile is read from HBM once per column tile.
+constexpr int kTileM = 128, kTileN = 128, kTileK = 32;
+constexpr int kTileStage = 3 * kTileM * kTileK * 2;   // A hi, A lo, W: 8 KiB each
+constexpr int kTileFinStride = kTileN + 4;            // floats per row of the epilogue tile
+
+__device__ __forceinline__ int tile_swz(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+
+template <GemmEpi E>
+__global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
+  constexpr int BM = kTileM, BN = kTileN, BK = kTileK, NT = 256;
+  constexpr bool kDual = E == GemmEpi::kSwiGLU;
+  constexpr int OC = kDual ? BN / 2 : BN;  // output columns of a tile (SwiGLU: 64 gate + 64 up rows)
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ float s_inv[BM];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nt = (slot / mtiles) * 8 + xcd, mt = slot % mtiles;
+  if (nt >= ntiles) return;
+  const int m0 = mt * BM, n0 = nt * OC;
+  const int K = g.K;
+  const bool norm = g.norm_w != nullptr;
+  auto src_row = [&](int m) {
+    return g.keep_bs > 0 ? (m / (g.keep_bs - 1)) * g.keep_bs + m % (g.keep_bs - 1) + 1 : m;
+  };
+  if (norm) {  // two threads per row sum the row's per-column-group sums of squares
+    const int row = threadIdx.x >> 1, sub = threadIdx.x & 1;
+    const int sr = src_row(min(m0 + row, g.M - 1));
+    float ss = 0.f;
+    for (int q = sub; q < g.ss_groups; q += 2) ss += g.ss[(size_t)q * g.ss_rows + sr];
+    ss += __shfl_xor(ss, 1, 64);
+    if (sub == 0) s_inv[row] = rsqrtf(ss / (float)K + g.eps);
+  }
+  // weight rows: DMA instruction j of this wave fills tile rows 16 (2 wave + j) + lane / 4; the
+  // lane's LDS slot holds chunk lane % 4 of the swizzled row, i.e. source chunk (lane % 4) ^ swz
+  const uint16_t *brow[2];
+  int bsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = (wave * 2 + j) * 16 + (lane >> 2);
+    const int wr = min(n0 + (kDual ? (r & (OC - 1)) : r), g.N - 1);
+    brow[j] = reinterpret_cast<const uint16_t *>(kDual ? g.b[r < OC ? 0 : 1] : g.b[0]) + (size_t)wr * K;
+    bsrc[j] = ((lane & 3) ^ ((r >> 2) & 3)) * 8;
+  }
+  // activation chunks: 8 fp32 of one row per chunk, two chunks per thread
+  const float *arow[2];
+  int ar[2], ac[2];
+  bool aok[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = threadIdx.x + j * NT;
+    ar[j] = q >> 2;
+    ac[j] = q & 3;
+    aok[j] = m0 + ar[j] < g.M;
+    arow[j] = reinterpret_cast<const float *>(g.a[0]) + (size_t)src_row(min(m0 + ar[j], g.M - 1)) * g.lda + ac[j] * 8;
+  }
+  Vec16 areg[2][2], wreg[2];
+  auto load_a = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      areg[j][0] = load_vec16(arow[j] + k0);
+      areg[j][1] = load_vec16(arow[j] + k0 + 4);
+      if (norm) wreg[j] = load_vec16(reinterpret_cast<const uint16_t *>(g.norm_w) + k0 + ac[j] * 8);
+    }
+  };
+  auto dma_w = [&](int k0, int st) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      dma16(brow[j] + k0 + bsrc[j], smem + st * kTileStage + 2 * BM * BK * 2 + (wave * 2 + j) * 1024);
+  };
+  auto store_a = [&](int k0, int st) {
+    unsigned char *sa = smem + st * kTileStage;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float f[8];
+      __builtin_memcpy(f, &areg[j][0].u, 16);
+      __builtin_memcpy(f + 4, &areg[j][1].u, 16);
+      if (norm) {
+        uint16_t w[8];
+        __builtin_memcpy(w, &wreg[j].u, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = f[e] * s_inv[ar[j]] * bf16_to_f32(w[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = aok[j] ? f[e] : 0.f;
+      if (g.a_out && nt == 0 && aok[j])
+#pragma unroll
+        for (int e = 0; e < 8; ++e) g.a_out[(size_t)(m0 + ar[j]) * K + k0 + ac[j] * 8 + e] = f[e];
+      uint16_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[e] = f32_to_bf16(f[e]);
+        lo[e] = f32_to_bf16(f[e] - bf16_to_f32(hi[e]));
+      }
+      const int o = tile_swz(ar[j], ac[j]);
+      __builtin_memcpy(sa + o, hi, 16);
+      __builtin_memcpy(sa + BM * BK * 2 + o, lo, 16);
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nk = K / BK;
+  load_a(0);
+  dma_w(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // s_inv
+  store_a(0, 0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int st = ks & 1;
+    if (ks + 1 < nk) {
+      load_a((ks + 1) * BK);
+      dma_w((ks + 1) * BK, st ^ 1);
+    }
+    const unsigned char *sa = smem + st * kTileStage;
+    const unsigned char *sw = sa + 2 * BM * BK * 2;
+    Vec16 bf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) bf[u].u = *reinterpret_cast<const uint4 *>(sw + tile_swz(wn * 64 + u * 16 + (lane & 15), lane >> 4));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int o = tile_swz(wm * 64 + t * 16 + (lane & 15), lane >> 4);
+      Vec16 ah, al;
+      ah.u = *reinterpret_cast<const uint4 *>(sa + o);
+      al.u = *reinterpret_cast<const uint4 *>(sa + BM * BK * 2 + o);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        mma16<uint16_t>(acc[t][u], ah, bf[u]);
+        mma16<uint16_t>(acc[t][u], al, bf[u]);
+      }
+    }
+    if (ks + 1 < nk) {
+      __builtin_amdgcn_s_waitcnt(0);  // the next step's activations (registers) and weights (DMA)
+      store_a((ks + 1) * BK, st ^ 1);
+    }
+    __syncthreads();
+  }
+
+  // ---- the tile through LDS: MFMA layout, lane holds rows (lane / 16) * 4 + i, column lane % 16
+  float *fin = reinterpret_cast<float *>(smem);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fin[(wm * 64 + t * 16 + (lane >> 4) * 4 + i) * kTileFinStride + wn * 64 + u * 16 + (lane & 15)] = acc[t][u][i];
+  __syncthreads();
+  if constexpr (E == GemmEpi::kStore || E == GemmEpi::kResidAdd) {
+    for (int e = threadIdx.x; e < BM * BN; e += NT) {
+      const int row = e / BN, col = e % BN;
+      const int m = m0 + row, n = n0 + col;
+      float v = fin[row * kTileFinStride + col];
+      if (m < g.M && n < g.N) {
+        const size_t o = (size_t)m * g.N + n;
+        if (E == GemmEpi::kResidAdd) v += g.out[o];
+        g.out[o] = v;
+      } else {
+        v = 0.f;
+      }
+      fin[row * kTileFinStride + col] = v * v;
+    }
+    if (g.ss_out) {  // per-row sum of squares over this column tile, for norm on load
+      __syncthreads();
+      const int row = threadIdx.x >> 1, sub = threadIdx.x & 1;
+      float sq = 0.f;
+      for (int c = sub; c < BN; c += 2) sq += fin[row * kTileFinStride + c];
+      sq += __shfl_xor(sq, 1, 64);
+      if (sub == 0 && m0 + row < g.M) g.ss_out[(size_t)nt * g.M + m0 + row] = sq;
+    }
+  } else if constexpr (E == GemmEpi::kSwiGLU) {
+    for (int e = threadIdx.x; e < BM * OC; e += NT) {
+      const int row = e / OC, col = e % OC;
+      const int m = m0 + row, n = n0 + col;
+      if (m < g.M && n < g.N) {
+        const float gt = fin[row * kTileFinStride + col], up = fin[row * kTileFinStride + OC + col];
+        g.out[(size_t)m * g.N + n] = gt / (1.f + expf(-gt)) * up;
+      }
+    }
+  } else if constexpr (E == GemmEpi::kArgmax) {
+    const int row = threadIdx.x >> 1, sub = threadIdx.x & 1;
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int c = sub; c < BN; c += 2)
+      if (n0 + c < g.N) argmax_merge(best, bi, fin[row * kTileFinStride + c], n0 + c);
+    const float ov = __shfl_xor(best, 1, 64);
+    const int oi = __shfl_xor(bi, 1, 64);
+    argmax_merge(best, bi, ov, oi);
+    if (sub == 0 && m0 + row < g.M) {
+      g.amax_val[(size_t)(m0 + row) * ntiles + nt] = best;
+      g.amax_idx[(size_t)(m0 + row) * ntiles + nt] = bi;
+    }
+  }
+}
+
+size_t tiled_lds_bytes() {
+  const size_t pipe = 2 * (size_t)kTileStage, fin = (size_t)kTileM * kTileFinStride * sizeof(float);
+  return pipe > fin ? pipe : fin;
+}
+
+template <GemmEpi E>
+hipError_t launch_tiled(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
+  auto kern = gemm_tiled_kernel<E>;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kMaxLds - 1024);
+  if (attr != hipSuccess) return attr;
+  const int ntiles = p.col_groups, mtiles = p.row_blocks;
+  kern<<<(ntiles + 7) / 8 * 8 * mtiles, 256, tiled_lds_bytes(), s>>>(g, mtiles, ntiles);
+  return hipGetLastError();
+}
+
 template <typename T, int MT, int CW, int CT, int KW, GemmEpi E, bool kAF32>
 size_t lds_bytes(const GemmArgs &g) {
   constexpr int KPV = Storage<T>::kPerVec;
@@ -727,8 +952,19 @@ int cu_count() {
 // down projection, fc over the concatenated target states), 4-wave work-groups (several per
 // CU) for gate|up, 4 wave columns x 2 K sub-slices otherwise. The head epilogues need
 // one head per column group.
-GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bool multi_a) {
+GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bool multi_a, bool a_f32) {
   GemmPlan p{};
+  // many rows: the LDS-tiled kernel (fp32 activations, bf16 weights; the store, residual,
+  // SwiGLU and argmax epilogues)
+  if (M > 64 && bf16 && a_f32 && !multi_a && K % kTileK == 0 &&
+      (epi == GemmEpi::kStore || epi == GemmEpi::kResidAdd || epi == GemmEpi::kSwiGLU || epi == GemmEpi::kArgmax)) {
+    p.tiled = 1;
+    p.cw = 8, p.ct = 1, p.kw = 1;
+    p.splits = 1;
+    p.col_groups = epi == GemmEpi::kSwiGLU ? (N + kTileN / 2 - 1) / (kTileN / 2) : (N + kTileN - 1) / kTileN;
+    p.row_blocks = (M + kTileM - 1) / kTileM;
+    return p;
+  }
   const bool head = epi == GemmEpi::kHeadNormRope || epi == GemmEpi::kKvScatter;
   const int mt = gemm_mt(M);
   if (head) {
@@ -775,6 +1011,20 @@ GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bo
 
 hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, const GemmPlan &p, hipStream_t s) {
   ProfScope prof(g0.tag ? g0.tag : "gemm", s);
+  if (p.tiled) {
+    const int oc = epi == GemmEpi::kSwiGLU ? kTileN / 2 : kTileN;
+    if (!bf16 || !g0.a_f32 || g0.a_nseg != 1 || g0.K % kTileK || g0.M < 1 || g0.keep_bs == 1 ||
+        ((g0.norm_w || g0.a_out) && !g0.ss) || p.col_groups != (g0.N + oc - 1) / oc ||
+        p.row_blocks != (g0.M + kTileM - 1) / kTileM)
+      return hipErrorInvalidValue;
+    switch (epi) {
+      case GemmEpi::kStore: return launch_tiled<GemmEpi::kStore>(g0, p, s);
+      case GemmEpi::kResidAdd: return launch_tiled<GemmEpi::kResidAdd>(g0, p, s);
+      case GemmEpi::kSwiGLU: return launch_tiled<GemmEpi::kSwiGLU>(g0, p, s);
+      case GemmEpi::kArgmax: return launch_tiled<GemmEpi::kArgmax>(g0, p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   const int step = p.kw * (bf16 ? ch_of<uint16_t>() : ch_of<float>());
   const int splits = p.splits;
   const bool head = epi == GemmEpi::kHeadNormRope || epi == GemmEpi::kKvScatter;

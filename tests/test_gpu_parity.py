@@ -44,6 +44,9 @@ def _compare_cache(spec, st, kc, vc, seqs):
     (SMALL_BF16, [300], 16, False),
     (SMALL_BF16, [0, 5, 64, 257], 16, True),
     (SMALL_BF16, [77, 130], 1, True),
+    # more than 64 rows: the LDS-tiled GEMM (80 rows: one ragged row tile; 144: two)
+    (SMALL_BF16, [10, 0, 77, 300, 5], 16, True),
+    (SMALL_BF16, [3, 40, 0, 129, 64, 1, 200, 17, 90], 16, True),
 ])
 def test_inject_and_propose_match_oracle(spec, ctx, P, shuffle):
     print(f"\n[case] spec={spec.dtype} H={spec.hidden} ctx={ctx} P={P}", flush=True)
