@@ -126,7 +126,7 @@ struct ProposePlan {
   GemmPlan qkv, o, gu, down, lm;
   int chunk, nsplit, n_ctr;
   size_t off_x, off_ss, off_part, off_ctr, off_q, off_k, off_v, off_o, off_act, off_po, off_pm, off_pl, off_amv,
-      off_ami, total;
+      off_ami, off_split, total;
 };
 
 ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
@@ -168,6 +168,13 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
   p.off_po = cv.take(nrow * D * sizeof(float));
   p.off_pm = cv.take(nrow * sizeof(float));
   p.off_pl = cv.take(nrow * sizeof(float));
+  // the (hi, lo) bf16 planes of the activations of the tiled GEMMs (many rows), reused by each
+  size_t split = 0;
+  if (p.o.tiled) split = std::max(split, (size_t)M * QH * D);
+  if (p.gu.tiled) split = std::max(split, (size_t)M * H);
+  if (p.down.tiled) split = std::max(split, (size_t)M * I);
+  if (p.lm.tiled) split = std::max(split, (size_t)std::max(p.Mk, 1) * H);
+  p.off_split = cv.take(2 * split * sizeof(uint16_t));
   p.off_amv = cv.take((size_t)p.lm.col_groups * std::max(p.Mk, 1) * sizeof(float));
   p.off_ami = cv.take((size_t)p.lm.col_groups * std::max(p.Mk, 1) * sizeof(int32_t));
   p.total = cv.off;
@@ -410,6 +417,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
   void *vb = at<char>(workspace, p.off_v);
   float *o = at<float>(workspace, p.off_o);
   float *act = at<float>(workspace, p.off_act);
+  uint16_t *asplit = at<uint16_t>(workspace, p.off_split);
 
   HIP_TRY(launch_embed(bf, w->embed, cfg->vocab, H, bonus_tokens, batch, bs, cfg->mask_token_id, x, ss, ctr, p.n_ctr,
                        s));
@@ -462,6 +470,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
 
     // O projection + residual add; the row sums of squares feed the post-attention norm
     GemmArgs go = gemm_args(cfg, "gemm.o", o, QH * D, M, H, QH * D, ctr, part);
+    go.a_split = asplit;
     go.b[0] = w->wo[l];
     go.b_end[0] = H;
     go.out = x;
@@ -471,6 +480,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
 
     // post_attention_layernorm on load; gate | up with SwiGLU
     GemmArgs gu = gemm_args(cfg, "gemm.gate_up", x, H, M, I, H, ctr, part);
+    gu.a_split = asplit;
     set_norm(gu, w->post_norm[l], ss, ss_groups, M);
     gu.b[0] = w->w_gate[l];
     gu.b[1] = w->w_up[l];
@@ -481,6 +491,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     HIP_TRY(launch_gemm(gu, bf, GemmEpi::kSwiGLU, p.gu, s));
 
     GemmArgs gd = gemm_args(cfg, "gemm.down", act, I, M, H, I, ctr, part);
+    gd.a_split = asplit;
     gd.b[0] = w->w_down[l];
     gd.b_end[0] = H;
     gd.out = x;
@@ -491,6 +502,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
 
   // final norm on load over the drafted rows (block slots 1..K); LM head + per-group argmax
   GemmArgs gl = gemm_args(cfg, "gemm.lm_head", x, H, p.Mk, cfg->vocab, H, ctr, part);
+  gl.a_split = asplit;
   set_norm(gl, w->final_norm, ss, ss_groups, M);
   gl.keep_bs = bs;
   gl.a_out = hidden_out;

@@ -31,6 +31,8 @@
 //    context K/V epilogue of injection (k_norm + RoPE + paged scatter). The last three
 //    need a column group to be exactly one head.
 // Up to 64 activation rows are held as MT accumulator tiles; more rows use grid.z blocks.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -623,48 +625,81 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
 
 // ---- Many rows (M > 64): LDS-tiled MFMA GEMM. A work-group computes a 128 x 128 tile of
 //      C = A W^T with 4 waves (2 x 2, 64 x 64 each, 4 x 4 MFMA tiles) and walks K in steps of
-//      32, double-buffered: the weight tile goes global -> LDS by DMA, the fp32 activation tile
-//      through registers, where it is normalised (norm on load) and split into the exact (hi,
-//      lo) bf16 pair; one step's loads are in flight while the previous step's 32 MFMAs per wave
-//      run. Both LDS tiles are [128 rows][32] bf16 with the 16-byte chunks of a row XOR-swizzled
+//      32. A first pass (split_rows_kernel) normalises the fp32 activation rows (norm on
+//      load) and splits them into the exact (hi, lo) pair of bf16 planes once, not once per
+//      column tile; the weight and activation tiles then go through registers into LDS, the
+//      loads of two steps in flight while a step's 32 MFMAs per wave run. The LDS tiles are [128 rows][32] bf16 with the 16-byte chunks of a row XOR-swizzled
 //      by (row / 4) % 4, so the 16 rows of a fragment read fall on distinct banks. The tile then
 //      goes through LDS to the epilogue (fp32 store / residual add with per-tile row sums of
 //      squares, SwiGLU, per-tile argmax). Work-group order puts every row tile of a column tile
 //      on one XCD, back to back, so the weight tile is read from HBM once per column tile.
 constexpr int kTileM = 128, kTileN = 128, kTileK = 32;
-constexpr int kTileStage = 3 * kTileM * kTileK * 2;   // A hi, A lo, W: 8 KiB each
+constexpr int kTileABytes = 2 * kTileM * kTileK * 2;  // A hi + A lo of one step (16 KiB)
+constexpr int kTileWBytes = kTileN * kTileK * 2;      // W of one step (8 KiB)
+constexpr int kTileW = 2 * kTileABytes;               // W slots follow the two A buffers
 constexpr int kTileFinStride = kTileN + 4;            // floats per row of the epilogue tile
 
 __device__ __forceinline__ int tile_swz(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
 
+// The activations of the tiled GEMM, once per launch: row m of A (the kept rows of the block
+// for the LM head), normalised when the GEMM norms on load (also written to a_out), split into
+// the exact pair of bf16 planes hi [M][K] and lo [M][K] (hi + lo = the fp32 value).
+__global__ __launch_bounds__(256) void split_rows_kernel(GemmArgs g, uint16_t *__restrict__ hi,
+                                                         uint16_t *__restrict__ lo) {
+  __shared__ float red[16];
+  const int m = blockIdx.x, K = g.K;
+  const int sr = g.keep_bs > 0 ? (m / (g.keep_bs - 1)) * g.keep_bs + m % (g.keep_bs - 1) + 1 : m;
+  const bool norm = g.norm_w != nullptr;
+  float inv = 1.f;
+  if (norm) {
+    float ss = 0.f;
+    for (int q = threadIdx.x; q < g.ss_groups; q += blockDim.x) ss += g.ss[(size_t)q * g.ss_rows + sr];
+    inv = rsqrtf(block_sum(ss, red) / (float)K + g.eps);
+  }
+  const float *a = reinterpret_cast<const float *>(g.a[0]) + (size_t)sr * g.lda;
+  for (int k = threadIdx.x * 8; k < K; k += blockDim.x * 8) {
+    float f[8];
+    const Vec16 v0 = load_vec16(a + k), v1 = load_vec16(a + k + 4);
+    __builtin_memcpy(f, &v0.u, 16);
+    __builtin_memcpy(f + 4, &v1.u, 16);
+    if (norm) {
+      const Vec16 wv = load_vec16(reinterpret_cast<const uint16_t *>(g.norm_w) + k);
+      uint16_t w[8];
+      __builtin_memcpy(w, &wv.u, 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = f[e] * inv * bf16_to_f32(w[e]);
+    }
+    if (g.a_out)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g.a_out[(size_t)m * K + k + e] = f[e];
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h[e] = f32_to_bf16(f[e]);
+      l[e] = f32_to_bf16(f[e] - bf16_to_f32(h[e]));
+    }
+    __builtin_memcpy(hi + (size_t)m * K + k, h, 16);
+    __builtin_memcpy(lo + (size_t)m * K + k, l, 16);
+  }
+}
+
+// A = the (hi, lo) planes from split_rows_kernel (g.a[0], g.a[1], row stride K).
 template <GemmEpi E>
 __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   constexpr int BM = kTileM, BN = kTileN, BK = kTileK, NT = 256;
   constexpr bool kDual = E == GemmEpi::kSwiGLU;
   constexpr int OC = kDual ? BN / 2 : BN;  // output columns of a tile (SwiGLU: 64 gate + 64 up rows)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ float s_inv[BM];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int nt = (slot / mtiles) * 8 + xcd, mt = slot % mtiles;
   if (nt >= ntiles) return;
   const int m0 = mt * BM, n0 = nt * OC;
   const int K = g.K;
-  const bool norm = g.norm_w != nullptr;
-  auto src_row = [&](int m) {
-    return g.keep_bs > 0 ? (m / (g.keep_bs - 1)) * g.keep_bs + m % (g.keep_bs - 1) + 1 : m;
-  };
-  if (norm) {  // two threads per row sum the row's per-column-group sums of squares
-    const int row = threadIdx.x >> 1, sub = threadIdx.x & 1;
-    const int sr = src_row(min(m0 + row, g.M - 1));
-    float ss = 0.f;
-    for (int q = sub; q < g.ss_groups; q += 2) ss += g.ss[(size_t)q * g.ss_rows + sr];
-    ss += __shfl_xor(ss, 1, 64);
-    if (sub == 0) s_inv[row] = rsqrtf(ss / (float)K + g.eps);
-  }
-  // weight rows: DMA instruction j of this wave fills tile rows 16 (2 wave + j) + lane / 4; the
-  // lane's LDS slot holds chunk lane % 4 of the swizzled row, i.e. source chunk (lane % 4) ^ swz
-  const uint16_t *brow[2];
+  // Loads of one K step, per thread: two 16-byte chunks of weight rows and two of activation
+  // rows (hi and lo each). Tile row r's chunk c is stored at tile_swz(r, c); thread slot
+  // (row 16 i + lane / 4, stored chunk lane % 4) holds source chunk (lane % 4) ^ swz(row).
+  const uint16_t *brow[2], *ahi[2], *alo[2];
   int bsrc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -672,60 +707,30 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
     const int wr = min(n0 + (kDual ? (r & (OC - 1)) : r), g.N - 1);
     brow[j] = reinterpret_cast<const uint16_t *>(kDual ? g.b[r < OC ? 0 : 1] : g.b[0]) + (size_t)wr * K;
     bsrc[j] = ((lane & 3) ^ ((r >> 2) & 3)) * 8;
+    const size_t arow = (size_t)min(m0 + r, g.M - 1) * K;  // rows past M: a valid row, never stored
+    ahi[j] = reinterpret_cast<const uint16_t *>(g.a[0]) + arow;
+    alo[j] = reinterpret_cast<const uint16_t *>(g.a[1]) + arow;
   }
-  // activation chunks: 8 fp32 of one row per chunk, two chunks per thread
-  const float *arow[2];
-  int ar[2], ac[2];
-  bool aok[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = threadIdx.x + j * NT;
-    ar[j] = q >> 2;
-    ac[j] = q & 3;
-    aok[j] = m0 + ar[j] < g.M;
-    arow[j] = reinterpret_cast<const float *>(g.a[0]) + (size_t)src_row(min(m0 + ar[j], g.M - 1)) * g.lda + ac[j] * 8;
-  }
-  Vec16 areg[2][2], wreg[2];
-  auto load_a = [&](int k0) {
+  // Two steps ahead: step s + 2 loads into register set s % 2 while step s computes; the LDS
+  // tiles are double buffered. Every iteration issues the same six loads (the K offset clamped
+  // past the end), so a fixed count of loads stays in flight. (No LDS DMA here: after one the
+  // compiler must assume every LDS read depends on it and waits for all loads in flight.)
+  Vec16 regs[2][3][2];  // [set][hi, lo, w][j]
+  auto load = [&](int set, int k0) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      areg[j][0] = load_vec16(arow[j] + k0);
-      areg[j][1] = load_vec16(arow[j] + k0 + 4);
-      if (norm) wreg[j] = load_vec16(reinterpret_cast<const uint16_t *>(g.norm_w) + k0 + ac[j] * 8);
+      regs[set][0][j] = load_vec16(ahi[j] + k0 + bsrc[j]);
+      regs[set][1][j] = load_vec16(alo[j] + k0 + bsrc[j]);
+      regs[set][2][j] = load_vec16(brow[j] + k0 + bsrc[j]);
     }
   };
-  auto dma_w = [&](int k0, int st) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      dma16(brow[j] + k0 + bsrc[j], smem + st * kTileStage + 2 * BM * BK * 2 + (wave * 2 + j) * 1024);
-  };
-  auto store_a = [&](int k0, int st) {
-    unsigned char *sa = smem + st * kTileStage;
+  auto store = [&](int set, int buf) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      float f[8];
-      __builtin_memcpy(f, &areg[j][0].u, 16);
-      __builtin_memcpy(f + 4, &areg[j][1].u, 16);
-      if (norm) {
-        uint16_t w[8];
-        __builtin_memcpy(w, &wreg[j].u, 16);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = f[e] * s_inv[ar[j]] * bf16_to_f32(w[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = aok[j] ? f[e] : 0.f;
-      if (g.a_out && nt == 0 && aok[j])
-#pragma unroll
-        for (int e = 0; e < 8; ++e) g.a_out[(size_t)(m0 + ar[j]) * K + k0 + ac[j] * 8 + e] = f[e];
-      uint16_t hi[8], lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hi[e] = f32_to_bf16(f[e]);
-        lo[e] = f32_to_bf16(f[e] - bf16_to_f32(hi[e]));
-      }
-      const int o = tile_swz(ar[j], ac[j]);
-      __builtin_memcpy(sa + o, hi, 16);
-      __builtin_memcpy(sa + BM * BK * 2 + o, lo, 16);
+      const int o = (wave * 2 + j) * 1024 + lane * 16;
+      *reinterpret_cast<uint4 *>(smem + buf * kTileABytes + o) = regs[set][0][j].u;
+      *reinterpret_cast<uint4 *>(smem + buf * kTileABytes + BM * BK * 2 + o) = regs[set][1][j].u;
+      *reinterpret_cast<uint4 *>(smem + kTileW + buf * kTileWBytes + o) = regs[set][2][j].u;
     }
   };
 
@@ -735,20 +740,19 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int nk = K / BK;
-  load_a(0);
-  dma_w(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // s_inv
-  store_a(0, 0);
+  auto kof = [&](int step) { return min(step, nk - 1) * BK; };
+  load(0, 0);
+  load(1, kof(1));
+  __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): step 0 has landed, step 1 in flight
+  store(0, 0);
   __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int st = ks & 1;
-    if (ks + 1 < nk) {
-      load_a((ks + 1) * BK);
-      dma_w((ks + 1) * BK, st ^ 1);
-    }
-    const unsigned char *sa = smem + st * kTileStage;
-    const unsigned char *sw = sa + 2 * BM * BK * 2;
+  // one K step; the register set is a compile-time constant (the loop is unrolled by two), so
+  // the loads stay in flight across the MFMAs instead of being waited for to index registers
+  auto step = [&](auto set_c, int ks) {
+    constexpr int set = decltype(set_c)::value;
+    load(set, kof(ks + 2));  // set ks % 2 held step ks, already in LDS
+    const unsigned char *sa = smem + set * kTileABytes;
+    const unsigned char *sw = smem + kTileW + set * kTileWBytes;
     Vec16 bf[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) bf[u].u = *reinterpret_cast<const uint4 *>(sw + tile_swz(wn * 64 + u * 16 + (lane & 15), lane >> 4));
@@ -764,12 +768,17 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
         mma16<uint16_t>(acc[t][u], al, bf[u]);
       }
     }
-    if (ks + 1 < nk) {
-      __builtin_amdgcn_s_waitcnt(0);  // the next step's activations (registers) and weights (DMA)
-      store_a((ks + 1) * BK, st ^ 1);
-    }
+    __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): step ks + 1's register set has landed
+    if (ks + 1 < nk) store(set ^ 1, set ^ 1);
     __syncthreads();
+  };
+  int ks = 0;
+  for (; ks + 1 < nk; ks += 2) {
+    step(std::integral_constant<int, 0>{}, ks);
+    step(std::integral_constant<int, 1>{}, ks + 1);
   }
+  if (ks < nk) step(std::integral_constant<int, 0>{}, ks);
+  __builtin_amdgcn_s_waitcnt(0);  // the clamped loads past the end
 
   // ---- the tile through LDS: MFMA layout, lane holds rows (lane / 16) * 4 + i, column lane % 16
   float *fin = reinterpret_cast<float *>(smem);
@@ -829,7 +838,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
 }
 
 size_t tiled_lds_bytes() {
-  const size_t pipe = 2 * (size_t)kTileStage, fin = (size_t)kTileM * kTileFinStride * sizeof(float);
+  const size_t pipe = (size_t)kTileW + 2 * kTileWBytes, fin = (size_t)kTileM * kTileFinStride * sizeof(float);
   return pipe > fin ? pipe : fin;
 }
 
@@ -841,7 +850,12 @@ hipError_t launch_tiled(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
                           kMaxLds - 1024);
   if (attr != hipSuccess) return attr;
   const int ntiles = p.col_groups, mtiles = p.row_blocks;
-  kern<<<(ntiles + 7) / 8 * 8 * mtiles, 256, tiled_lds_bytes(), s>>>(g, mtiles, ntiles);
+  uint16_t *hi = g.a_split, *lo = g.a_split + (size_t)g.M * g.K;
+  split_rows_kernel<<<g.M, 256, 0, s>>>(g, hi, lo);
+  GemmArgs t = g;
+  t.a[0] = hi;
+  t.a[1] = lo;
+  kern<<<(ntiles + 7) / 8 * 8 * mtiles, 256, tiled_lds_bytes(), s>>>(t, mtiles, ntiles);
   return hipGetLastError();
 }
 
@@ -1013,7 +1027,7 @@ hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, const GemmPla
   ProfScope prof(g0.tag ? g0.tag : "gemm", s);
   if (p.tiled) {
     const int oc = epi == GemmEpi::kSwiGLU ? kTileN / 2 : kTileN;
-    if (!bf16 || !g0.a_f32 || g0.a_nseg != 1 || g0.K % kTileK || g0.M < 1 || g0.keep_bs == 1 ||
+    if (!bf16 || !g0.a_f32 || g0.a_nseg != 1 || !g0.a_split || g0.K % kTileK || g0.M < 1 || g0.keep_bs == 1 ||
         ((g0.norm_w || g0.a_out) && !g0.ss) || p.col_groups != (g0.N + oc - 1) / oc ||
         p.row_blocks != (g0.M + kTileM - 1) / kTileM)
       return hipErrorInvalidValue;

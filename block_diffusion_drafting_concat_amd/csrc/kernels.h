@@ -83,6 +83,7 @@ struct GemmArgs {
   void *v_cache[64];
   const char *tag;  // name under which the launch is timed when profiling is on
   int kt, kp;       // set by launch_gemm: K per split, K per staged LDS pass
+  uint16_t *a_split;  // tiled plans: workspace for the (hi, lo) bf16 planes of A, 2 * M * K
 };
 
 int gemm_mt(int M);
