@@ -98,7 +98,7 @@ int gemm_tiles(const GemmPlan &p) { return p.col_groups * p.row_blocks; }
 struct InjectPlan {
   int rows, n_ctr;
   GemmPlan fc, kv;
-  size_t off_y, off_ss, off_part, off_ctr, total;
+  size_t off_y, off_ss, off_part, off_ctr, off_split, total;
 };
 
 InjectPlan plan_inject(const dflash_config *c, int rows) {
@@ -107,7 +107,7 @@ InjectPlan plan_inject(const dflash_config *c, int rows) {
   const bool bf = is_bf16(c);
   const int H = c->hidden, D = c->head_dim;
   const int kvn = std::max(c->n_layers * 2 * c->n_kv_heads * D, 16);
-  p.fc = gemm_plan(rows, H, c->n_aux * c->target_hidden, D, bf, GemmEpi::kStore, c->n_aux > 1, false);
+  p.fc = gemm_plan(rows, H, c->n_aux * c->target_hidden, D, bf, GemmEpi::kStore, c->n_aux > 1, false, c->n_aux);
   p.kv = gemm_plan(rows, kvn, H, D, bf, GemmEpi::kKvScatter, false);
   p.n_ctr = std::max(gemm_tiles(p.fc), gemm_tiles(p.kv));
   const size_t part = std::max(gemm_part_floats(p.fc, rows, H, GemmEpi::kStore),
@@ -117,6 +117,8 @@ InjectPlan plan_inject(const dflash_config *c, int rows) {
   p.off_ss = cv.take((size_t)p.fc.col_groups * rows * sizeof(float));
   p.off_part = cv.take(part * sizeof(float));
   p.off_ctr = cv.take((size_t)p.n_ctr * sizeof(unsigned));
+  // the (hi, lo) bf16 planes of the normalised context rows when the K/V projection is tiled
+  p.off_split = cv.take(p.kv.tiled ? 2 * (size_t)rows * H * sizeof(uint16_t) : 0);
   p.total = cv.off;
   return p;
 }
@@ -170,6 +172,7 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
   p.off_pl = cv.take(nrow * sizeof(float));
   // the (hi, lo) bf16 planes of the activations of the tiled GEMMs (many rows), reused by each
   size_t split = 0;
+  if (p.qkv.tiled) split = std::max(split, (size_t)M * H);
   if (p.o.tiled) split = std::max(split, (size_t)M * QH * D);
   if (p.gu.tiled) split = std::max(split, (size_t)M * H);
   if (p.down.tiled) split = std::max(split, (size_t)M * I);
@@ -356,6 +359,7 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
 
     // hidden_norm on load; K/V of every layer in one projection; k_norm + RoPE + scatter
     GemmArgs k = gemm_args(cfg, "gemm.kv", y, H, rows, kvn, H, ctr, part);
+    k.a_split = at<uint16_t>(workspace, p.off_split);
     set_norm(k, w->hidden_norm, ss, p.fc.col_groups, rows);
     k.b[0] = w->kv_fused;
     k.b_end[0] = kvn;
@@ -425,6 +429,7 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
   for (int l = 0; l < L; ++l) {
     // input_layernorm on load; q | k | v in one pass; q/k norm + RoPE in the epilogue
     GemmArgs g = gemm_args(cfg, "gemm.qkv", x, H, M, (QH + 2 * KVH) * D, H, ctr, part);
+    g.a_split = asplit;
     set_norm(g, w->in_norm[l], ss, ss_groups, M);
     g.b[0] = w->wq[l];
     g.b[1] = w->wk[l];

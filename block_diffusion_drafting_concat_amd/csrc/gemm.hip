@@ -84,6 +84,54 @@ __device__ __forceinline__ void head_norm_rope(float &x1, float &x2, bool own, i
   x2 = b * cs + a * sn;
 }
 
+// The head epilogues on head h of output row m, one head vector per wave: lane i < D/2 owns
+// the pair (x1, x2) = (i, i + D/2); every lane of the wave takes part (the norm is a wave sum).
+//  kHeadNormRope: h indexes q | k | v heads of the block; q and k heads are RMS-normalised
+//                 (q_norm / k_norm) and rotated at position min(seq_len, max_ctx) + j of
+//                 block slot j; all are rounded to the storage type into q, k or v.
+//  kKvScatter:    h indexes layer-major (k heads, v heads) of the fused context projection;
+//                 keys take the layer's k_norm and RoPE at positions[m]; both are rounded and
+//                 written to slot slot_mapping[m] of the layer's cache (a slot outside
+//                 [0, num_slots) is skipped).
+template <typename T, GemmEpi E>
+__device__ __forceinline__ void head_epilogue(const GemmArgs &g, int h, int m, float x1, float x2, bool own, int i1,
+                                              int D) {
+  const int half = D / 2, i2 = i1 + half;
+  T *dst;
+  if constexpr (E == GemmEpi::kHeadNormRope) {
+    const int QH = g.n_q_heads, KVH = g.n_kv_heads;
+    if (h < QH + KVH) {
+      const T *w = reinterpret_cast<const T *>(h < QH ? g.q_norm : g.k_norm);
+      const int b = m / g.block_size, j = m % g.block_size;
+      const int pos = min(min(max(g.seq_lens[b], 0), g.max_ctx) + j, g.rope_max_pos - 1);
+      head_norm_rope(x1, x2, own, D, Storage<T>::load(w, i1), Storage<T>::load(w, i2), g.eps,
+                     g.rope_cos[(size_t)pos * half + i1], g.rope_sin[(size_t)pos * half + i1]);
+      dst = h < QH ? reinterpret_cast<T *>(g.q) + ((size_t)m * QH + h) * D
+                   : reinterpret_cast<T *>(g.k) + ((size_t)m * KVH + h - QH) * D;
+    } else {
+      dst = reinterpret_cast<T *>(g.v) + ((size_t)m * KVH + h - QH - KVH) * D;
+    }
+  } else {
+    const int KVH = g.n_kv_heads;
+    const int l = h / (2 * KVH), j = h % (2 * KVH);
+    const bool is_v = j >= KVH;
+    const int gh = is_v ? j - KVH : j;
+    const int64_t slot = g.slot_mapping[m];
+    if (slot < 0 || slot >= g.num_slots) return;  // padding row / out of range: skipped (uniform per wave)
+    if (!is_v) {
+      const T *w = reinterpret_cast<const T *>(g.layer_k_norm[l]);
+      const int pos = min(max(g.positions[m], 0), g.rope_max_pos - 1);
+      head_norm_rope(x1, x2, own, D, Storage<T>::load(w, i1), Storage<T>::load(w, i2), g.eps,
+                     g.rope_cos[(size_t)pos * half + i1], g.rope_sin[(size_t)pos * half + i1]);
+    }
+    dst = reinterpret_cast<T *>(is_v ? g.v_cache[l] : g.k_cache[l]) + ((size_t)slot * KVH + gh) * D;
+  }
+  if (own) {
+    Storage<T>::store(dst, i1, x1);
+    Storage<T>::store(dst, i2, x2);
+  }
+}
+
 // Occupancy at one row tile: 4-wave work-groups run four to a CU, 8-wave ones two (at most
 // 128 VGPRs); a work-group that owns several column groups keeps their accumulators and has
 // the CU alone.
@@ -572,51 +620,13 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
       }
     } else if constexpr (E == GemmEpi::kHeadNormRope || E == GemmEpi::kKvScatter) {
       // one head per column group; one wave per row; lane i < D/2 owns the pair (i, i + D/2)
-      const int D = TC, half = TC / 2;
+      const int half = TC / 2;
       const bool own = lane < half;
-      const int i1 = own ? lane : 0, i2 = i1 + half;
-      const int h = cg;
+      const int i1 = own ? lane : 0;
       for (int row = wave; row < TR; row += NW) {
         const int m = m0 + row;
         if (m >= g.M) break;
-        float x1 = fin[row * TC + i1], x2 = fin[row * TC + i2];
-        if constexpr (E == GemmEpi::kHeadNormRope) {
-          const int QH = g.n_q_heads, KVH = g.n_kv_heads;
-          T *dst;
-          if (h < QH + KVH) {
-            const T *w = reinterpret_cast<const T *>(h < QH ? g.q_norm : g.k_norm);
-            const int b = m / g.block_size, j = m % g.block_size;
-            const int pos = min(min(max(g.seq_lens[b], 0), g.max_ctx) + j, g.rope_max_pos - 1);
-            head_norm_rope(x1, x2, own, D, Storage<T>::load(w, i1), Storage<T>::load(w, i2), g.eps,
-                           g.rope_cos[(size_t)pos * half + i1], g.rope_sin[(size_t)pos * half + i1]);
-            dst = h < QH ? reinterpret_cast<T *>(g.q) + ((size_t)m * QH + h) * D
-                         : reinterpret_cast<T *>(g.k) + ((size_t)m * KVH + h - QH) * D;
-          } else {
-            dst = reinterpret_cast<T *>(g.v) + ((size_t)m * KVH + h - QH - KVH) * D;
-          }
-          if (own) {
-            Storage<T>::store(dst, i1, x1);
-            Storage<T>::store(dst, i2, x2);
-          }
-        } else {
-          const int KVH = g.n_kv_heads;
-          const int l = h / (2 * KVH), j = h % (2 * KVH);
-          const bool is_v = j >= KVH;
-          const int gh = is_v ? j - KVH : j;
-          const int64_t slot = g.slot_mapping[m];
-          if (slot < 0 || slot >= g.num_slots) continue;  // padding row / out of range: skipped
-          if (!is_v) {
-            const T *w = reinterpret_cast<const T *>(g.layer_k_norm[l]);
-            const int pos = min(max(g.positions[m], 0), g.rope_max_pos - 1);
-            head_norm_rope(x1, x2, own, D, Storage<T>::load(w, i1), Storage<T>::load(w, i2), g.eps,
-                           g.rope_cos[(size_t)pos * half + i1], g.rope_sin[(size_t)pos * half + i1]);
-          }
-          T *dst = reinterpret_cast<T *>(is_v ? g.v_cache[l] : g.k_cache[l]) + ((size_t)slot * KVH + gh) * D;
-          if (own) {
-            Storage<T>::store(dst, i1, x1);
-            Storage<T>::store(dst, i2, x2);
-          }
-        }
+        head_epilogue<T, E>(g, cg, m, fin[row * TC + i1], fin[row * TC + i1 + half], own, i1, TC);
       }
     }
   }  // column groups of this work-group
@@ -683,8 +693,10 @@ __global__ __launch_bounds__(256) void split_rows_kernel(GemmArgs g, uint16_t *_
   }
 }
 
-// A = the (hi, lo) planes from split_rows_kernel (g.a[0], g.a[1], row stride K).
-template <GemmEpi E>
+// kLo: A = the (hi, lo) planes from split_rows_kernel (g.a[0], g.a[1], row stride K), two
+// MFMAs per step. Otherwise A is bf16 as given (the auxiliary target states): g.a_nseg equal
+// K segments g.a[s] with row stride g.lda, each a multiple of the K step, one MFMA per step.
+template <GemmEpi E, bool kLo>
 __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   constexpr int BM = kTileM, BN = kTileN, BK = kTileK, NT = 256;
   constexpr bool kDual = E == GemmEpi::kSwiGLU;
@@ -696,20 +708,28 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
   if (nt >= ntiles) return;
   const int m0 = mt * BM, n0 = nt * OC;
   const int K = g.K;
+  constexpr int NLD = kLo ? 3 : 2;  // 16-byte loads per chunk slot and K step: (hi, lo,) w
+  const int kseg = K / g.a_nseg;    // bf16 A: K columns per segment
   // Loads of one K step, per thread: two 16-byte chunks of weight rows and two of activation
   // rows (hi and lo each). Tile row r's chunk c is stored at tile_swz(r, c); thread slot
   // (row 16 i + lane / 4, stored chunk lane % 4) holds source chunk (lane % 4) ^ swz(row).
   const uint16_t *brow[2], *ahi[2], *alo[2];
+  size_t aoff[2];
   int bsrc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = (wave * 2 + j) * 16 + (lane >> 2);
-    const int wr = min(n0 + (kDual ? (r & (OC - 1)) : r), g.N - 1);
-    brow[j] = reinterpret_cast<const uint16_t *>(kDual ? g.b[r < OC ? 0 : 1] : g.b[0]) + (size_t)wr * K;
+    // weight row of tile row r (a row past N reads a valid row; its results are never stored)
+    const int n = min(n0 + (kDual ? (r & (OC - 1)) : r), g.N - 1);
+    int seg = 0, nbase = 0;
+    if (!kDual)
+      while (seg < g.b_nseg - 1 && n >= g.b_end[seg]) nbase = g.b_end[seg++];
+    brow[j] = reinterpret_cast<const uint16_t *>(kDual ? g.b[r < OC ? 0 : 1] : g.b[seg]) + (size_t)(n - nbase) * K;
     bsrc[j] = ((lane & 3) ^ ((r >> 2) & 3)) * 8;
-    const size_t arow = (size_t)min(m0 + r, g.M - 1) * K;  // rows past M: a valid row, never stored
-    ahi[j] = reinterpret_cast<const uint16_t *>(g.a[0]) + arow;
-    alo[j] = reinterpret_cast<const uint16_t *>(g.a[1]) + arow;
+    const int am = min(m0 + r, g.M - 1);  // rows past M: a valid row, never stored
+    aoff[j] = (size_t)am * (kLo ? (size_t)K : (size_t)g.lda);
+    ahi[j] = reinterpret_cast<const uint16_t *>(g.a[0]) + aoff[j];
+    alo[j] = reinterpret_cast<const uint16_t *>(g.a[kLo ? 1 : 0]) + aoff[j];
   }
   // Two steps ahead: step s + 2 loads into register set s % 2 while step s computes; the LDS
   // tiles are double buffered. Every iteration issues the same six loads (the K offset clamped
@@ -717,10 +737,18 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
   // compiler must assume every LDS read depends on it and waits for all loads in flight.)
   Vec16 regs[2][3][2];  // [set][hi, lo, w][j]
   auto load = [&](int set, int k0) {
+    if constexpr (!kLo) {  // the segment of the concatenated A holding columns [k0, k0 + BK)
+      const int seg = k0 / kseg;
+      const uint16_t *a0 = reinterpret_cast<const uint16_t *>(g.a[seg]) + (k0 - seg * kseg);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) regs[set][0][j] = load_vec16(a0 + aoff[j] + bsrc[j]);
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      regs[set][0][j] = load_vec16(ahi[j] + k0 + bsrc[j]);
-      regs[set][1][j] = load_vec16(alo[j] + k0 + bsrc[j]);
+      if constexpr (kLo) {
+        regs[set][0][j] = load_vec16(ahi[j] + k0 + bsrc[j]);
+        regs[set][1][j] = load_vec16(alo[j] + k0 + bsrc[j]);
+      }
       regs[set][2][j] = load_vec16(brow[j] + k0 + bsrc[j]);
     }
   };
@@ -729,10 +757,12 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
     for (int j = 0; j < 2; ++j) {
       const int o = (wave * 2 + j) * 1024 + lane * 16;
       *reinterpret_cast<uint4 *>(smem + buf * kTileABytes + o) = regs[set][0][j].u;
-      *reinterpret_cast<uint4 *>(smem + buf * kTileABytes + BM * BK * 2 + o) = regs[set][1][j].u;
+      if constexpr (kLo) *reinterpret_cast<uint4 *>(smem + buf * kTileABytes + BM * BK * 2 + o) = regs[set][1][j].u;
       *reinterpret_cast<uint4 *>(smem + kTileW + buf * kTileWBytes + o) = regs[set][2][j].u;
     }
   };
+  // vmcnt(NLD * 2): the newest step's loads may stay in flight
+  constexpr unsigned kWaitOlder = 0x0F70u | (unsigned)(NLD * 2);
 
   f32x4_t acc[4][4];
 #pragma unroll
@@ -743,7 +773,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
   auto kof = [&](int step) { return min(step, nk - 1) * BK; };
   load(0, 0);
   load(1, kof(1));
-  __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): step 0 has landed, step 1 in flight
+  __builtin_amdgcn_s_waitcnt(kWaitOlder);  // step 0 has landed, step 1 in flight
   store(0, 0);
   __syncthreads();
   // one K step; the register set is a compile-time constant (the loop is unrolled by two), so
@@ -761,14 +791,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
       const int o = tile_swz(wm * 64 + t * 16 + (lane & 15), lane >> 4);
       Vec16 ah, al;
       ah.u = *reinterpret_cast<const uint4 *>(sa + o);
-      al.u = *reinterpret_cast<const uint4 *>(sa + BM * BK * 2 + o);
+      if constexpr (kLo) al.u = *reinterpret_cast<const uint4 *>(sa + BM * BK * 2 + o);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         mma16<uint16_t>(acc[t][u], ah, bf[u]);
-        mma16<uint16_t>(acc[t][u], al, bf[u]);
+        if constexpr (kLo) mma16<uint16_t>(acc[t][u], al, bf[u]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): step ks + 1's register set has landed
+    __builtin_amdgcn_s_waitcnt(kWaitOlder);  // step ks + 1's register set has landed
     if (ks + 1 < nk) store(set ^ 1, set ^ 1);
     __syncthreads();
   };
@@ -834,6 +864,17 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
       g.amax_val[(size_t)(m0 + row) * ntiles + nt] = best;
       g.amax_idx[(size_t)(m0 + row) * ntiles + nt] = bi;
     }
+  } else {  // head epilogues: BN / D heads per tile row, one (row, head) per wave at a time
+    const int D = g.head_dim, half = D / 2, hpt = BN / D;
+    const bool own = lane < half;
+    const int i1 = own ? lane : 0;
+    for (int q = wave; q < BM * hpt; q += NT / 64) {
+      const int row = q / hpt, hh = q % hpt, m = m0 + row;
+      if (m >= g.M) break;
+      if (n0 + hh * D >= g.N) continue;
+      head_epilogue<uint16_t, E>(g, n0 / D + hh, m, fin[row * kTileFinStride + hh * D + i1],
+                                 fin[row * kTileFinStride + hh * D + i1 + half], own, i1, D);
+    }
   }
 }
 
@@ -842,19 +883,22 @@ size_t tiled_lds_bytes() {
   return pipe > fin ? pipe : fin;
 }
 
-template <GemmEpi E>
+template <GemmEpi E, bool kLo>
 hipError_t launch_tiled(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
-  auto kern = gemm_tiled_kernel<E>;
+  auto kern = gemm_tiled_kernel<E, kLo>;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           kMaxLds - 1024);
   if (attr != hipSuccess) return attr;
   const int ntiles = p.col_groups, mtiles = p.row_blocks;
-  uint16_t *hi = g.a_split, *lo = g.a_split + (size_t)g.M * g.K;
-  split_rows_kernel<<<g.M, 256, 0, s>>>(g, hi, lo);
   GemmArgs t = g;
-  t.a[0] = hi;
-  t.a[1] = lo;
+  if constexpr (kLo) {
+    uint16_t *hi = g.a_split, *lo = g.a_split + (size_t)g.M * g.K;
+    split_rows_kernel<<<g.M, 256, 0, s>>>(g, hi, lo);
+    t.a[0] = hi;
+    t.a[1] = lo;
+    t.a_nseg = 1;
+  }
   kern<<<(ntiles + 7) / 8 * 8 * mtiles, 256, tiled_lds_bytes(), s>>>(t, mtiles, ntiles);
   return hipGetLastError();
 }
@@ -966,12 +1010,15 @@ int cu_count() {
 // down projection, fc over the concatenated target states), 4-wave work-groups (several per
 // CU) for gate|up, 4 wave columns x 2 K sub-slices otherwise. The head epilogues need
 // one head per column group.
-GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bool multi_a, bool a_f32) {
+GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bool multi_a, bool a_f32,
+                   int a_segs) {
   GemmPlan p{};
-  // many rows: the LDS-tiled kernel (fp32 activations, bf16 weights; the store, residual,
-  // SwiGLU and argmax epilogues)
-  if (M > 64 && bf16 && a_f32 && !multi_a && K % kTileK == 0 &&
-      (epi == GemmEpi::kStore || epi == GemmEpi::kResidAdd || epi == GemmEpi::kSwiGLU || epi == GemmEpi::kArgmax)) {
+  // many rows: the LDS-tiled kernel (bf16 weights; fp32 activations, or bf16 ones in
+  // segments of whole K steps; a head epilogue needs whole heads in a column tile)
+  const bool head_fits = (epi != GemmEpi::kHeadNormRope && epi != GemmEpi::kKvScatter) ||
+                         ((head_dim == 64 || head_dim == 128) && N % head_dim == 0);
+  if (M > 64 && bf16 && K % kTileK == 0 && (a_f32 ? !multi_a : (K / a_segs) % kTileK == 0 && K % a_segs == 0) &&
+      head_fits) {
     p.tiled = 1;
     p.cw = 8, p.ct = 1, p.kw = 1;
     p.splits = 1;
@@ -1027,15 +1074,23 @@ hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, const GemmPla
   ProfScope prof(g0.tag ? g0.tag : "gemm", s);
   if (p.tiled) {
     const int oc = epi == GemmEpi::kSwiGLU ? kTileN / 2 : kTileN;
-    if (!bf16 || !g0.a_f32 || g0.a_nseg != 1 || !g0.a_split || g0.K % kTileK || g0.M < 1 || g0.keep_bs == 1 ||
-        ((g0.norm_w || g0.a_out) && !g0.ss) || p.col_groups != (g0.N + oc - 1) / oc ||
-        p.row_blocks != (g0.M + kTileM - 1) / kTileM)
+    const bool head = epi == GemmEpi::kHeadNormRope || epi == GemmEpi::kKvScatter;
+    const bool a_ok = g0.a_f32 ? g0.a_nseg == 1 && g0.a_split && (!(g0.norm_w || g0.a_out) || g0.ss)
+                               : epi == GemmEpi::kStore && g0.a_nseg >= 1 && g0.a_nseg <= 8 &&
+                                     g0.K % g0.a_nseg == 0 && (g0.K / g0.a_nseg) % kTileK == 0 && !g0.norm_w &&
+                                     !g0.a_out && g0.keep_bs == 0 && g0.lda % 8 == 0;
+    if (!bf16 || !a_ok || g0.K % kTileK || g0.M < 1 || g0.keep_bs == 1 || p.col_groups != (g0.N + oc - 1) / oc ||
+        p.row_blocks != (g0.M + kTileM - 1) / kTileM || g0.b_nseg < 1 || g0.b_nseg > 3 ||
+        (head && ((g0.head_dim != 64 && g0.head_dim != 128) || g0.N % g0.head_dim)))
       return hipErrorInvalidValue;
     switch (epi) {
-      case GemmEpi::kStore: return launch_tiled<GemmEpi::kStore>(g0, p, s);
-      case GemmEpi::kResidAdd: return launch_tiled<GemmEpi::kResidAdd>(g0, p, s);
-      case GemmEpi::kSwiGLU: return launch_tiled<GemmEpi::kSwiGLU>(g0, p, s);
-      case GemmEpi::kArgmax: return launch_tiled<GemmEpi::kArgmax>(g0, p, s);
+      case GemmEpi::kStore:
+        return g0.a_f32 ? launch_tiled<GemmEpi::kStore, true>(g0, p, s) : launch_tiled<GemmEpi::kStore, false>(g0, p, s);
+      case GemmEpi::kResidAdd: return launch_tiled<GemmEpi::kResidAdd, true>(g0, p, s);
+      case GemmEpi::kSwiGLU: return launch_tiled<GemmEpi::kSwiGLU, true>(g0, p, s);
+      case GemmEpi::kArgmax: return launch_tiled<GemmEpi::kArgmax, true>(g0, p, s);
+      case GemmEpi::kHeadNormRope: return launch_tiled<GemmEpi::kHeadNormRope, true>(g0, p, s);
+      case GemmEpi::kKvScatter: return launch_tiled<GemmEpi::kKvScatter, true>(g0, p, s);
       default: return hipErrorInvalidValue;
     }
   }

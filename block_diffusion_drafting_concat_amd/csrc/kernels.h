@@ -100,8 +100,10 @@ struct GemmPlan {
   int col_groups, row_blocks;  // output tiles = col_groups * row_blocks (split-K counters)
   int tiled;                   // 1: the LDS-tiled kernel for many rows (128 x 128 output tiles)
 };
-// a_f32: the activations are fp32 rows (else the storage type, as the auxiliary target states)
-GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bool multi_a, bool a_f32 = true);
+// a_f32: the activations are fp32 rows (else the storage type, as the auxiliary target states,
+// in a_segs equal K segments)
+GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bool multi_a, bool a_f32 = true,
+                   int a_segs = 1);
 hipError_t launch_gemm(const GemmArgs &g, bool bf16, GemmEpi epi, const GemmPlan &p, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------

@@ -13,6 +13,11 @@ SMALL_BF16 = synth.DrafterSpec(hidden=256, n_layers=2, n_q_heads=8, n_kv_heads=2
                                intermediate=512, vocab=2048, n_aux=2, target_hidden=192, block_size=16,
                                mask_token_id=2047, rope_theta=1e6, dtype="bf16")
 TINY = synth.WORKLOADS["tiny_fp32_b1"].spec
+# head_dim 64 (two heads per 128-column tile of the tiled GEMM), four auxiliary segments of
+# 96 columns (three K steps each), a ragged vocabulary tile (1008)
+SMALL_BF16_D64 = synth.DrafterSpec(hidden=384, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                                   intermediate=384, vocab=1008, n_aux=4, target_hidden=96, block_size=8,
+                                   mask_token_id=1007, rope_theta=1e4, dtype="bf16")
 
 
 def _compare_drafts(spec, got_ids, got_drafts, ref, bonus, what):
@@ -47,6 +52,7 @@ def _compare_cache(spec, st, kc, vc, seqs):
     # more than 64 rows: the LDS-tiled GEMM (80 rows: one ragged row tile; 144: two)
     (SMALL_BF16, [10, 0, 77, 300, 5], 16, True),
     (SMALL_BF16, [3, 40, 0, 129, 64, 1, 200, 17, 90], 16, True),
+    (SMALL_BF16_D64, [70, 3, 150, 0, 33, 90, 12, 20, 64, 100], 16, True),
 ])
 def test_inject_and_propose_match_oracle(spec, ctx, P, shuffle):
     print(f"\n[case] spec={spec.dtype} H={spec.hidden} ctx={ctx} P={P}", flush=True)
