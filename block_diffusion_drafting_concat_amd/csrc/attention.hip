@@ -5,8 +5,10 @@
 // its bs*G query rows (the G q-heads sharing kv head g, times the bs block positions) share
 // every K/V tile it loads, so each KV byte is read from HBM once per work-group. The key
 // range c_b + bs is cut into splits of `chunk` keys so that one long context (32k) still
-// spreads over the whole chip; split partials (unnormalised output, running max, running
-// sum) are merged by a second kernel with the usual log-sum-exp rescaling.
+// spreads over the whole chip, and so that many contexts of unequal length give even
+// work-groups. A second kernel merges the split partials (unnormalised output, running max,
+// running sum) with the usual log-sum-exp rescaling; a sequence with one split normalises in
+// place.
 //
 // MFMA layout. Scores are computed transposed, S^T = K Q^T (A = K tile rows, B = Q rows), so
 // each lane ends up holding 4 keys of one query row. The output is computed as O^T = V^T P^T,
@@ -70,53 +72,95 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const T *vbk = reinterpret_cast<const T *>(a.vb);
   const int32_t *bt = a.block_table + (size_t)b * a.maxb;
 
-  // The page of each key this thread stages, read for a whole tile ahead: the page-table
-  // reads depend only on the key index (clamped into the table), not on the context length,
-  // so the first tile's go out together with the length and the queries.
-  constexpr int kVecPerThread = kTileKeys * CPR / 256;
-  static_assert(kTileKeys * CPR % 256 == 0, "staging vectors per thread");
-  int pages[kVecPerThread];
+  // Staging of a 64-key tile. K: item v = (key v / CPR, 16-byte part v % CPR), one row-major
+  // vector write each. V is stored transposed (vts[d][key]) by items of two consecutive keys
+  // (2 kappa, 2 kappa + 1) and one part: the pair of values of each d goes out as one 4-byte
+  // (bf16) or 8-byte (fp32) write. Within a wave, 16 consecutive kappa x 4 parts write each
+  // row, so a write instruction touches at most two rows that share banks.
+  // The loads of tile t + 1 are in registers while tile t is computed, and the page-table
+  // entries they need are read a tile earlier still: page reads depend only on the key index
+  // (clamped into the table), never on the context length.
+  constexpr int KVEC = kTileKeys * CPR / 256;  // K items per thread
+  constexpr int VVEC = (kTileKeys / 2) * CPR / 256;  // V items per thread
+  static_assert(kTileKeys * CPR % 256 == 0 && (kTileKeys / 2) * CPR % 256 == 0, "staging items per thread");
+  auto v_kappa = [](int v) { return (v & 15) | (((v >> 6) & 1) << 4); };
+  auto v_part = [](int v) { return ((v >> 4) & 3) | ((v >> 7) << 2); };
+  int kpg[KVEC], vpg[VVEC][2];
+  Vec16 kreg[KVEC], vreg[VVEC][2];
   auto load_pages = [&](int t0) {
 #pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
+    for (int i = 0; i < KVEC; ++i) {
       const int t = t0 + ((int)threadIdx.x + i * 256) / CPR;
-      pages[i] = bt[min(t / a.P, a.maxb - 1)];
+      kpg[i] = bt[min(t / a.P, a.maxb - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < VVEC; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = t0 + 2 * v_kappa((int)threadIdx.x + i * 256) + h;
+        vpg[i][h] = bt[min(t / a.P, a.maxb - 1)];
+      }
+  };
+  // source of key t (part `part`) in the context cache or the block's own k / v
+  auto key_off = [&](int t, int page, int part, bool &ctx) {
+    ctx = t < c;
+    if (ctx) return ((size_t)(min(max(page, 0), a.num_pages - 1) * a.P + t % a.P) * a.KVH + g) * D + part * KPV;
+    return ((size_t)(b * a.bs + (t - c)) * a.KVH + g) * D + part * KPV;
+  };
+  auto issue = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < KVEC; ++i) {
+      const int v = threadIdx.x + i * 256, t = t0 + v / CPR;
+      bool ctx;
+      const size_t off = key_off(t, kpg[i], v % CPR, ctx);
+      kreg[i] = t < kend ? load_vec16((ctx ? kc : kbk) + off) : zero_vec16();
+    }
+#pragma unroll
+    for (int i = 0; i < VVEC; ++i) {
+      const int v = threadIdx.x + i * 256;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = t0 + 2 * v_kappa(v) + h;
+        bool ctx;
+        const size_t off = key_off(t, vpg[i][h], v_part(v), ctx);
+        vreg[i][h] = t < kend ? load_vec16((ctx ? vc : vbk) + off) : zero_vec16();
+      }
     }
   };
   load_pages(kbeg);
+  issue(kbeg);
+  if (kbeg + kTileKeys < kend) load_pages(kbeg + kTileKeys);
 
   for (int t0 = kbeg; t0 < kend; t0 += kTileKeys) {
-    // ---- stage the K tile (row-major) and V tile (transposed) in LDS
+    // ---- the tile's registers into LDS: K row-major, V transposed
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
+    for (int i = 0; i < KVEC; ++i) {
       const int v = threadIdx.x + i * 256;
-      const int key = v / CPR, part = v % CPR;
-      const int t = t0 + key;
-      Vec16 kv = zero_vec16(), vv = zero_vec16();
-      if (t < kend) {
-        const T *ksrc, *vsrc;
-        if (t < c) {
-          const int page = min(max(pages[i], 0), a.num_pages - 1);
-          const size_t off = ((size_t)(page * a.P + t % a.P) * a.KVH + g) * D + part * KPV;
-          ksrc = kc + off;
-          vsrc = vc + off;
-        } else {
-          const size_t off = ((size_t)(b * a.bs + (t - c)) * a.KVH + g) * D + part * KPV;
-          ksrc = kbk + off;
-          vsrc = vbk + off;
-        }
-        kv = load_vec16(ksrc);
-        vv = load_vec16(vsrc);
-      }
-      *reinterpret_cast<uint4 *>(&ks[key * KSTR + part * KPV]) = kv.u;
-      T ve[KPV];
-      __builtin_memcpy(ve, &vv.u, 16);
-#pragma unroll
-      for (int e = 0; e < KPV; ++e) vts[(part * KPV + e) * VSTR + key] = ve[e];
+      *reinterpret_cast<uint4 *>(&ks[(v / CPR) * KSTR + (v % CPR) * KPV]) = kreg[i].u;
     }
-    if (t0 + kTileKeys < kend) load_pages(t0 + kTileKeys);  // in flight during this tile
+#pragma unroll
+    for (int i = 0; i < VVEC; ++i) {
+      const int v = threadIdx.x + i * 256, kap = v_kappa(v), part = v_part(v);
+      T v0[KPV], v1[KPV];
+      __builtin_memcpy(v0, &vreg[i][0].u, 16);
+      __builtin_memcpy(v1, &vreg[i][1].u, 16);
+#pragma unroll
+      for (int e = 0; e < KPV; ++e) {
+        T *dst = &vts[(part * KPV + e) * VSTR + 2 * kap];
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint32_t *>(dst) = uint32_t(v0[e]) | (uint32_t(v1[e]) << 16);
+        } else {
+          *reinterpret_cast<float2 *>(dst) = make_float2(v0[e], v1[e]);
+        }
+      }
+    }
     __syncthreads();
+    // ---- the next tile's loads fly during this tile's compute
+    if (t0 + kTileKeys < kend) {
+      issue(t0 + kTileKeys);
+      if (t0 + 2 * kTileKeys < kend) load_pages(t0 + 2 * kTileKeys);
+    }
     if (wave * 16 >= R) continue;
 
     // ---- S^T tiles: 4 tiles of 16 keys; tile sb row rho holds key
@@ -195,11 +239,29 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       }
     }
   }
-  if (wave * 16 >= R) return;
+  // ---- O^T lane layout: d = db*16 + (lane/16)*4 + i, row r = wave*16 + lane%16
+  const bool active = wave * 16 < R;
+  if (active) {
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+  }
+  const int G2 = a.QH / a.KVH;
+  auto out_row = [&](int row) {  // merged output row of query row `row` = hh*bs + j
+    return a.o + ((size_t)(b * a.bs + row % a.bs) * a.QH + g * G2 + row / a.bs) * D;
+  };
+  const int ns = (T_total + a.chunk - 1) / a.chunk;  // splits of this sequence
+  if (ns == 1) {  // the whole key range: normalise in place
+    if (rvalid) {
+      const float inv = 1.f / l_run;
+      float *op = out_row(r) + (lane >> 4) * 4;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4_t *>(op + db * 16) = acc_o[db] * inv;
+    }
+    return;
+  }
 
-  // ---- partials: O^T lane layout is d = db*16 + (lane/16)*4 + i, row = lane%16
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  // ---- split partials (unnormalised output, running max, running sum), merged by the next
+  //      launch
   const size_t base = ((size_t)(b * a.KVH + g) * a.nsplit + split) * 64;
   if (rvalid) {
     float *po = a.po + (base + r) * D + (lane >> 4) * 4;
@@ -212,12 +274,58 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split partials of one (sequence, kv head, query row). Thread (d, sub) sums the
-// splits s = sub (mod 256 / D) for element d with the split weights exp2(m_s - max m); the
+// Merge of up to 16 splits per sequence: thread (query row, d) of a (sequence, kv head),
+// 256 / D rows per work-group. The split weights are exp2(m_s - max m); the loads of 16 splits are in flight
+// together, and the sums run in split order.
+template <typename T>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  const int D = a.D, rpw = 256 / D;
+  const int row = blockIdx.x * rpw + (int)threadIdx.x / D, d = threadIdx.x % D;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int G = a.QH / a.KVH;
+  if (row >= a.bs * G) return;
+  const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
+  const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
+  if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel
+  const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64 + row;
+  const float *pm = a.pm + base, *pl = a.pl + base, *po = a.po + base * D + d;
+  float mmax = -INFINITY;
+  for (int s0 = 0; s0 < ns; s0 += 16) {
+    float mv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) mv[u] = pm[(size_t)min(s0 + u, ns - 1) * 64];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) mmax = fmaxf(mmax, mv[u]);
+  }
+  float num = 0.f, den = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 16) {
+    float pv[16], mv[16], lv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const size_t q = (size_t)min(s0 + u, ns - 1) * 64;
+      pv[u] = po[q * D];
+      mv[u] = pm[q];
+      lv[u] = pl[q];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (s0 + u < ns) {
+        const float w = exp2f(mv[u] - mmax);
+        num += w * pv[u];
+        den += w * lv[u];
+      }
+  }
+  const int hh = row / a.bs, j = row % a.bs;
+  a.o[((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d] = num / den;
+}
+
+// Merge of many splits (more than 16 per sequence: one long context): work-group = one
+// (sequence, kv head, query row). Thread (d, sub) sums the splits s = sub (mod 256 / D) for
+// element d with the split weights exp2(m_s - max m); the
 // loads of 16 splits are issued together, and the sub-sums are combined through LDS in a
 // fixed order.
 template <typename T>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_merge_rows_kernel(AttnArgs a) {
   __shared__ float red[4];
   __shared__ float rnum[256];
   __shared__ float rden[4];
@@ -227,6 +335,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int d = threadIdx.x % D, sub = threadIdx.x / D;
   const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
+  if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel
   const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64 + row;
   float mloc = -INFINITY;
   for (int s = threadIdx.x; s < ns; s += 256) mloc = fmaxf(mloc, a.pm[base + (size_t)s * 64]);
@@ -276,11 +385,14 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
       attn_partial_kernel<T, 64><<<grid, 256, 0, s>>>(a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int G = a.QH / a.KVH;
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const int R = a.bs * (a.QH / a.KVH), rpw = 256 / a.D;
   {
     ProfScope prof("attn_merge", s);
-    attn_merge_kernel<T><<<dim3(a.bs * G, a.KVH, a.B), 256, 0, s>>>(a);
+    if (a.nsplit > 16)
+      attn_merge_rows_kernel<T><<<dim3(R, a.KVH, a.B), 256, 0, s>>>(a);
+    else
+      attn_merge_kernel<T><<<dim3((R + rpw - 1) / rpw, a.KVH, a.B), 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
@@ -288,10 +400,12 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 }  // namespace
 
 void attn_plan(int B, int KVH, int max_keys, int *chunk, int *nsplit) {
-  // Aim for ~1024 work-groups in total, in splits of at least one 64-key tile.
+  // Aim for ~1024 work-groups in total, in splits of at least one 64-key tile and at most
+  // eight: with many sequences of unequal length, short splits keep the work-groups even.
   long want = (long)max_keys * B * KVH / 1024;
   int ch = (int)((want + kTileKeys - 1) / kTileKeys) * kTileKeys;
   if (ch < kTileKeys) ch = kTileKeys;
+  if (ch > 8 * kTileKeys) ch = 8 * kTileKeys;
   *chunk = ch;
   *nsplit = (max_keys + ch - 1) / ch;
 }

@@ -53,6 +53,8 @@ def _compare_cache(spec, st, kc, vc, seqs):
     (SMALL_BF16, [10, 0, 77, 300, 5], 16, True),
     (SMALL_BF16, [3, 40, 0, 129, 64, 1, 200, 17, 90], 16, True),
     (SMALL_BF16_D64, [70, 3, 150, 0, 33, 90, 12, 20, 64, 100], 16, True),
+    # every sequence within one 64-key attention split: normalised in place, no merge launch
+    (SMALL_BF16, [0, 20, 3, 40], 16, True),
 ])
 def test_inject_and_propose_match_oracle(spec, ctx, P, shuffle):
     print(f"\n[case] spec={spec.dtype} H={spec.hidden} ctx={ctx} P={P}", flush=True)
