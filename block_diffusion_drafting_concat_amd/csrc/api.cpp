@@ -91,7 +91,9 @@ constexpr int kInjectChunk = 4096;  // rows per injection pass
 
 // fp32 partial buffer of a GEMM (split-K only).
 size_t gemm_part_floats(const GemmPlan &p, int M, int N, GemmEpi e) {
-  return p.splits > 1 ? (size_t)p.splits * M * N * (e == GemmEpi::kSwiGLU ? 2 : 1) : 0;
+  if (p.splits <= 1) return 0;
+  if (p.tiled) return (size_t)p.splits * p.row_blocks * p.col_groups * 128 * 128;  // whole 128 x 128 tiles
+  return (size_t)p.splits * M * N * (e == GemmEpi::kSwiGLU ? 2 : 1);
 }
 int gemm_tiles(const GemmPlan &p) { return p.col_groups * p.row_blocks; }
 
@@ -147,11 +149,13 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
   p.down = gemm_plan(M, H, I, D, bf, GemmEpi::kResidAdd, false);
   p.lm = gemm_plan(std::max(p.Mk, 1), c->vocab, H, D, bf, GemmEpi::kArgmax, false);
   attn_plan(B, KVH, max_ctx + c->block_size, &p.chunk, &p.nsplit);
-  p.n_ctr = std::max(std::max(gemm_tiles(p.qkv), gemm_tiles(p.o)), std::max(gemm_tiles(p.gu), gemm_tiles(p.down)));
-  const size_t part = std::max(std::max(gemm_part_floats(p.qkv, M, nqkv, GemmEpi::kHeadNormRope),
-                                        gemm_part_floats(p.o, M, H, GemmEpi::kResidAdd)),
-                               std::max(gemm_part_floats(p.gu, M, I, GemmEpi::kSwiGLU),
-                                        gemm_part_floats(p.down, M, H, GemmEpi::kResidAdd)));
+  p.n_ctr = std::max(std::max(std::max(gemm_tiles(p.qkv), gemm_tiles(p.o)), std::max(gemm_tiles(p.gu), gemm_tiles(p.down))),
+                     gemm_tiles(p.lm));
+  const size_t part = std::max(std::max(std::max(gemm_part_floats(p.qkv, M, nqkv, GemmEpi::kHeadNormRope),
+                                                 gemm_part_floats(p.o, M, H, GemmEpi::kResidAdd)),
+                                        std::max(gemm_part_floats(p.gu, M, I, GemmEpi::kSwiGLU),
+                                                 gemm_part_floats(p.down, M, H, GemmEpi::kResidAdd))),
+                               gemm_part_floats(p.lm, std::max(p.Mk, 1), c->vocab, GemmEpi::kArgmax));
   // the residual-stream producers (O and down projections) write one sum of squares per
   // column group; the embedding writes one
   const int ss_groups = std::max(std::max(p.o.col_groups, p.down.col_groups), 1);

@@ -697,14 +697,17 @@ __global__ __launch_bounds__(256) void split_rows_kernel(GemmArgs g, uint16_t *_
 // MFMAs per step. Otherwise A is bf16 as given (the auxiliary target states): g.a_nseg equal
 // K segments g.a[s] with row stride g.lda, each a multiple of the K step, one MFMA per step.
 template <GemmEpi E, bool kLo>
-__global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
+__global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int splits) {
   constexpr int BM = kTileM, BN = kTileN, BK = kTileK, NT = 256;
   constexpr bool kDual = E == GemmEpi::kSwiGLU;
   constexpr int OC = kDual ? BN / 2 : BN;  // output columns of a tile (SwiGLU: 64 gate + 64 up rows)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ unsigned s_flag;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  // work-group -> (column tile, row tile, K split): consecutive work-groups of one XCD (ids
+  // congruent mod 8) walk the row tiles and splits of one column tile
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int nt = (slot / mtiles) * 8 + xcd, mt = slot % mtiles;
+  const int nt = (slot / (mtiles * splits)) * 8 + xcd, mt = slot % mtiles, sp = (slot / mtiles) % splits;
   if (nt >= ntiles) return;
   const int m0 = mt * BM, n0 = nt * OC;
   const int K = g.K;
@@ -769,9 +772,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int nk = K / BK;
-  auto kof = [&](int step) { return min(step, nk - 1) * BK; };
-  load(0, 0);
+  // this split's K steps [ks0, ks0 + nk) of the K / BK (splits of near-equal length)
+  const int ks0 = (int)((long)sp * (K / BK) / splits), nk = (int)((long)(sp + 1) * (K / BK) / splits) - ks0;
+  auto kof = [&](int step) { return (ks0 + min(step, nk - 1)) * BK; };
+  load(0, kof(0));
   load(1, kof(1));
   __builtin_amdgcn_s_waitcnt(kWaitOlder);  // step 0 has landed, step 1 in flight
   store(0, 0);
@@ -820,6 +824,42 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
       for (int i = 0; i < 4; ++i)
         fin[(wm * 64 + t * 16 + (lane >> 4) * 4 + i) * kTileFinStride + wn * 64 + u * 16 + (lane & 15)] = acc[t][u][i];
   __syncthreads();
+  // ---- split-K: every split stores its tile ([split][row tile][column tile] blocks of
+  //      BM x BN in the workspace) and the last to arrive sums all splits in split order, with
+  //      the device-scope relaxed atomic accesses and store-complete-before-arrival protocol of
+  //      the streaming kernel.
+  if (splits > 1) {
+    const size_t tstride = (size_t)mtiles * ntiles * BM * BN;
+    const size_t tbase = ((size_t)mt * ntiles + nt) * BM * BN;
+    float *mine = g.part + (size_t)sp * tstride + tbase;
+    for (int e = threadIdx.x; e < BM * BN; e += NT)
+      __hip_atomic_store(mine + e, fin[(e / BN) * kTileFinStride + e % BN], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
+    __syncthreads();
+    unsigned *ctr = g.counters + (size_t)mt * ntiles + nt;
+    if (threadIdx.x == 0) s_flag = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_flag != (unsigned)(splits - 1)) return;  // another split finishes this tile
+    for (int e = threadIdx.x; e < BM * BN; e += NT) {
+      const float *src = g.part + tbase + e;
+      float sum = 0.f;
+      for (int q0 = 0; q0 < splits; q0 += 4) {  // loads of 4 splits in flight, summed in split order
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[u] = q0 + u < splits ? __hip_atomic_load(src + (size_t)(q0 + u) * tstride, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (q0 + u < splits) sum += v[u];
+      }
+      fin[(e / BN) * kTileFinStride + e % BN] = sum;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  }
   if constexpr (E == GemmEpi::kStore || E == GemmEpi::kResidAdd) {
     for (int e = threadIdx.x; e < BM * BN; e += NT) {
       const int row = e / BN, col = e % BN;
@@ -899,7 +939,7 @@ hipError_t launch_tiled(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
     t.a[1] = lo;
     t.a_nseg = 1;
   }
-  kern<<<(ntiles + 7) / 8 * 8 * mtiles, 256, tiled_lds_bytes(), s>>>(t, mtiles, ntiles);
+  kern<<<(ntiles + 7) / 8 * 8 * mtiles * p.splits, 256, tiled_lds_bytes(), s>>>(t, mtiles, ntiles, p.splits);
   return hipGetLastError();
 }
 
@@ -1021,9 +1061,21 @@ GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bo
       head_fits) {
     p.tiled = 1;
     p.cw = 8, p.ct = 1, p.kw = 1;
-    p.splits = 1;
     p.col_groups = epi == GemmEpi::kSwiGLU ? (N + kTileN / 2 - 1) / (kTileN / 2) : (N + kTileN - 1) / kTileN;
     p.row_blocks = (M + kTileM - 1) / kTileM;
+    // Split-K when there are fewer tiles than CUs: the split count minimising the rounds (of
+    // one work-group per CU: a second one on a CU shares its LDS and matrix cores and adds
+    // little) per unit of work, plus a small cost per extra split for the reduction through
+    // the workspace; at least 32 K steps per split.
+    const long wgs = (long)p.col_groups * p.row_blocks, slots = cu_count();
+    p.splits = 1;
+    if (wgs < slots) {
+      double best = 1.0;
+      for (int s = 2; s <= 8 && 32 * s <= K / kTileK; ++s) {
+        const double cost = (double)((wgs * s + slots - 1) / slots) / s + 0.03 * (s - 1);
+        if (cost < best - 1e-9) best = cost, p.splits = s;
+      }
+    }
     return p;
   }
   const bool head = epi == GemmEpi::kHeadNormRope || epi == GemmEpi::kKvScatter;
@@ -1080,7 +1132,8 @@ hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, const GemmPla
                                      g0.K % g0.a_nseg == 0 && (g0.K / g0.a_nseg) % kTileK == 0 && !g0.norm_w &&
                                      !g0.a_out && g0.keep_bs == 0 && g0.lda % 8 == 0;
     if (!bf16 || !a_ok || g0.K % kTileK || g0.M < 1 || g0.keep_bs == 1 || p.col_groups != (g0.N + oc - 1) / oc ||
-        p.row_blocks != (g0.M + kTileM - 1) / kTileM || g0.b_nseg < 1 || g0.b_nseg > 3 ||
+        p.row_blocks != (g0.M + kTileM - 1) / kTileM || g0.b_nseg < 1 || g0.b_nseg > 3 || p.splits < 1 ||
+        p.splits > g0.K / kTileK || (p.splits > 1 && (!g0.part || !g0.counters)) ||
         (head && ((g0.head_dim != 64 && g0.head_dim != 128) || g0.N % g0.head_dim)))
       return hipErrorInvalidValue;
     switch (epi) {
