@@ -28,7 +28,7 @@ namespace {
 constexpr int kTileKeys = 64;
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 3) void attn_partial_kernel(AttnArgs a) {
   constexpr int KPV = Storage<T>::kPerVec;
   constexpr int CH = 4 * KPV;                // contraction elements per MFMA step
   constexpr int NB = KPV / 4;                // score tiles per P.V step
