@@ -30,7 +30,9 @@ import torch  # noqa: E402
 from block_diffusion_drafting_concat_amd import binding, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-# GEMM kernel instances (by epilogue) and the profiling tags of their launches in a step.
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix-core peak
+# GEMM kernel instances (by epilogue) and the profiling tags of their launches in a batch-1
+# step (16 block rows: the weight-streaming kernel).
 GEMM_KERNELS = {
     "gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=1,NCG=1,kHeadNormRope,fp32-A>": ("gemm.qkv",),
     "gemm_kernel<bf16,MT=1,CW=4,CT=1,KW=2,NCG=1,kResidAdd,fp32-A>": ("gemm.o",),
@@ -39,6 +41,16 @@ GEMM_KERNELS = {
     "gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=1,NCG=8,kArgmax,fp32-A>": ("gemm.lm_head",),
     "gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=2,NCG=1,kStore,multi-A>": ("gemm.fc",),
     "gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=1,NCG=1,kKvScatter,fp32-A>": ("gemm.kv",),
+}
+# More than 64 rows (batch 32 and 128): the LDS-tiled kernel, one instance per epilogue
+# (fc reads the auxiliary states as bf16, every other projection fp32 activations as hi + lo).
+TILED_KERNELS = {
+    "gemm_tiled_kernel<kHeadNormRope,hi+lo-A>": ("gemm.qkv",),
+    "gemm_tiled_kernel<kResidAdd,hi+lo-A>": ("gemm.o", "gemm.down"),
+    "gemm_tiled_kernel<kSwiGLU,hi+lo-A>": ("gemm.gate_up",),
+    "gemm_tiled_kernel<kArgmax,hi+lo-A>": ("gemm.lm_head",),
+    "gemm_tiled_kernel<kStore,bf16-A>": ("gemm.fc",),
+    "gemm_tiled_kernel<kKvScatter,hi+lo-A>": ("gemm.kv",),
 }
 GEMM_SOURCES = ("block_diffusion_drafting_concat_amd/csrc/gemm.hip", "block_diffusion_drafting_concat_amd/csrc/common.h")
 
@@ -302,24 +314,30 @@ def main():
     prof_all = binding.profile_collect()
     n_prof = max(5, args.steps // 5)
 
-    def per_kernel_of(prof):
-        out = {}
-        for kname, tags in GEMM_KERNELS.items():
-            n = sum(prof.get(t, (0, 0.0))[0] for t in tags)
-            ms = sum(prof.get(t, (0, 0.0))[1] for t in tags)
-            nbytes = sum(tag_bytes(spec, t, *roles[t], es) * prof.get(t, (0, 0.0))[0] for t in tags)
-            out[kname] = (n, ms, nbytes)
-        return out
-
     B, K = bench.B, spec.block_size - 1
     es = 2 if spec.dtype == "bf16" else 4
     roles = gemm_roles(spec, B * spec.block_size, B * wl.inject_rows)
+    # batch 1: weight-streaming kernels priced against HBM; more than 64 block rows: the tiled
+    # kernels, priced against the bf16 matrix cores by their algorithmic flops (2 M N K)
+    tiled = B * spec.block_size > 64 and spec.dtype == "bf16"
+    kernels = TILED_KERNELS if tiled else GEMM_KERNELS
+
+    def per_kernel_of(prof):
+        out = {}
+        for kname, tags in kernels.items():
+            n = sum(prof.get(t, (0, 0.0))[0] for t in tags)
+            ms = sum(prof.get(t, (0, 0.0))[1] for t in tags)
+            nbytes = sum(tag_bytes(spec, t, *roles[t], es) * prof.get(t, (0, 0.0))[0] for t in tags)
+            flops = sum(2.0 * roles[t][0] * roles[t][1] * roles[t][2] * prof.get(t, (0, 0.0))[0] for t in tags)
+            out[kname] = (n, ms, nbytes, flops)
+        return out
+
     pk_all = per_kernel_of(prof_all)
     dom = max(pk_all, key=lambda k: pk_all[k][1])
 
     # timed region: events only around the dominant kernel's launches
     binding.profile_reset()
-    binding.profile_filter(GEMM_KERNELS[dom])
+    binding.profile_filter(kernels[dom])
     binding.profile_enable(True)
     sec = bench.timed(args.steps)
     binding.profile_enable(False)
@@ -362,9 +380,24 @@ def main():
                   "rate": st[2] / st[1] if st[1] else None, "length": 1 + st[2] / st[0] if st[0] else None,
                   "note": "device counters fused into verify, on synthetic target tokens (a sanity check, not a "
                           "model's acceptance)"}
-    g_launch, g_ms, g_bytes = per_kernel_of(prof)[dom]
+    g_launch, g_ms, g_bytes, g_flops = per_kernel_of(prof)[dom]
     achieved = g_bytes / (g_ms * 1e-3) / 1e9 if g_ms > 0 else 0.0
     traffic = load_traffic(dom, wl.name)
+    if tiled:
+        roofline = {"bound": "mfma", "kernel": dom,
+                    "achieved": g_flops / (g_ms * 1e-3) / 1e12 if g_ms > 0 else 0.0,
+                    "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "traffic": traffic, "launches": g_launch,
+                    "avg_launch_us": (g_ms / g_launch * 1e3) if g_launch else None,
+                    "algorithmic_flops_per_launch": g_flops / g_launch if g_launch else None,
+                    "note": "algorithmic flops 2MNK; the fp32 activations enter the bf16 MFMA as a hi + lo pair, "
+                            "so the matrix cores execute twice these flops"}
+        roofline["frac"] = roofline["achieved"] / MFMA_BF16_PEAK_TFS
+    else:
+        roofline = {"bound": "hbm", "kernel": dom,
+                    "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": traffic, "launches": g_launch,
+                    "avg_launch_us": (g_ms / g_launch * 1e3) if g_launch else None,
+                    "algorithmic_bytes_per_launch": g_bytes / g_launch if g_launch else None}
     sbytes = step_bytes(spec, B, bench.ctx, wl.inject_rows)
     result = {
         "metric": "drafted tokens/sec and draft blocks/sec (Qwen3-8B-shape, b16); % HBM/MFMA roofline",
@@ -393,14 +426,11 @@ def main():
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": sbytes,
                           "achieved": sbytes / (sec_graph if sec_graph else sec) / 1e9, "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": sbytes / (sec_graph if sec_graph else sec) / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "kernel": dom,
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "launches": g_launch,
-                     "avg_launch_us": (g_ms / g_launch * 1e3) if g_launch else None,
-                     "algorithmic_bytes_per_launch": g_bytes / g_launch if g_launch else None},
+        "roofline": roofline,
         "kernel_ms_per_step_all_events": {k: v[1] / n_prof for k, v in sorted(prof_all.items())},
         "gemm_kernels_all_events": {k: {"launches_per_step": v[0] / n_prof, "ms_per_step": v[1] / n_prof,
-                                        "achieved_GBs": v[2] / (v[1] * 1e-3) / 1e9 if v[1] else None}
+                                        "achieved_GBs": v[2] / (v[1] * 1e-3) / 1e9 if v[1] else None,
+                                        "achieved_TFs": v[3] / (v[1] * 1e-3) / 1e12 if v[1] else None}
                                     for k, v in pk_all.items()},
     }
     if not args.no_cpu_baseline:

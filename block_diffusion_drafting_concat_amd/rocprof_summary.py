@@ -45,6 +45,9 @@ def short_name(name: str) -> str:
              f"NCG={m.group(6)},{EPI[m.group(7)]}")
         s += ",multi-A" if m.group(8) == "true" else ""
         return s + (",fp32-A>" if m.group(9) == "true" else ">")
+    m = re.search(r"gemm_tiled_kernel<\(dflash::GemmEpi\)(\d), (true|false)>", name)
+    if m:
+        return f"gemm_tiled_kernel<{EPI[m.group(1)]},{'hi+lo-A' if m.group(2) == 'true' else 'bf16-A'}>"
     name = re.sub(r"^void ", "", name)
     name = name.replace("dflash::(anonymous namespace)::", "")
     return re.sub(r"\(.*$", "", name)
@@ -82,7 +85,7 @@ def pmc(workload: str, fetch_csv: str, write_csv: str) -> dict:
     kernels = {}
     for k in set(f) | set(w):
         s = short_name(k)
-        if not s.startswith("gemm_kernel") and not s.startswith("attn_"):
+        if not s.startswith("gemm_") and not s.startswith("attn_"):
             continue
         fk = sum(f.get(k, [0])) / max(1, len(f.get(k, [])))
         wk = sum(w.get(k, [0])) / max(1, len(w.get(k, [])))
