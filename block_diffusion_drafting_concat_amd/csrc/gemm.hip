@@ -638,11 +638,15 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
 //      32. A first pass (split_rows_kernel) normalises the fp32 activation rows (norm on
 //      load) and splits them into the exact (hi, lo) pair of bf16 planes once, not once per
 //      column tile; the weight and activation tiles then go through registers into LDS, the
-//      loads of two steps in flight while a step's 32 MFMAs per wave run. The LDS tiles are [128 rows][32] bf16 with the 16-byte chunks of a row XOR-swizzled
-//      by (row / 4) % 4, so the 16 rows of a fragment read fall on distinct banks. The tile then
-//      goes through LDS to the epilogue (fp32 store / residual add with per-tile row sums of
-//      squares, SwiGLU, per-tile argmax). Work-group order puts every row tile of a column tile
-//      on one XCD, back to back, so the weight tile is read from HBM once per column tile.
+//      loads of two steps in flight while a step's 32 MFMAs per wave run. The LDS tiles are
+//      [128 rows][32] bf16 with the 16-byte chunks of a row XOR-swizzled by (row / 4) % 4, so
+//      the 16 rows of a fragment read fall on distinct banks. The tile then goes through LDS to
+//      the epilogue in two halves of 64 rows (fp32 store / residual add with per-tile row sums
+//      of squares, SwiGLU, per-tile argmax, the head epilogues), which keeps a work-group at
+//      48 KiB of LDS: three fit on a CU. With fewer tiles than CUs, K is split over
+//      work-groups and the last split of a tile reduces. Work-group order puts every row tile
+//      (and split) of a column tile on one XCD, back to back, so the weight tile is read from
+//      HBM once per column tile.
 constexpr int kTileM = 128, kTileN = 128, kTileK = 32;
 constexpr int kTileABytes = 2 * kTileM * kTileK * 2;  // A hi + A lo of one step (16 KiB)
 constexpr int kTileWBytes = kTileN * kTileK * 2;      // W of one step (8 KiB)
@@ -697,7 +701,7 @@ __global__ __launch_bounds__(256) void split_rows_kernel(GemmArgs g, uint16_t *_
 // MFMAs per step. Otherwise A is bf16 as given (the auxiliary target states): g.a_nseg equal
 // K segments g.a[s] with row stride g.lda, each a multiple of the K step, one MFMA per step.
 template <GemmEpi E, bool kLo>
-__global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int splits) {
+__global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int splits) {
   constexpr int BM = kTileM, BN = kTileN, BK = kTileK, NT = 256;
   constexpr bool kDual = E == GemmEpi::kSwiGLU;
   constexpr int OC = kDual ? BN / 2 : BN;  // output columns of a tile (SwiGLU: 64 gate + 64 up rows)
@@ -814,112 +818,135 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs g, int mtil
   if (ks < nk) step(std::integral_constant<int, 0>{}, ks);
   __builtin_amdgcn_s_waitcnt(0);  // the clamped loads past the end
 
-  // ---- the tile through LDS: MFMA layout, lane holds rows (lane / 16) * 4 + i, column lane % 16
+  // ---- the tile through LDS in two halves of 64 rows (the waves with wm == h own half h),
+  //      so the epilogue needs half the LDS of the tile and three work-groups fit on a CU.
+  //      MFMA layout: lane holds rows (lane / 16) * 4 + i, column lane % 16.
+  constexpr int HM = BM / 2;
   float *fin = reinterpret_cast<float *>(smem);
+  auto acc_to_fin = [&](int h) {
+    if (wm == h)
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fin[(wm * 64 + t * 16 + (lane >> 4) * 4 + i) * kTileFinStride + wn * 64 + u * 16 + (lane & 15)] = acc[t][u][i];
-  __syncthreads();
+          for (int i = 0; i < 4; ++i)
+            fin[(t * 16 + (lane >> 4) * 4 + i) * kTileFinStride + wn * 64 + u * 16 + (lane & 15)] = acc[t][u][i];
+  };
   // ---- split-K: every split stores its tile ([split][row tile][column tile] blocks of
   //      BM x BN in the workspace) and the last to arrive sums all splits in split order, with
   //      the device-scope relaxed atomic accesses and store-complete-before-arrival protocol of
   //      the streaming kernel.
+  const size_t tstride = (size_t)mtiles * ntiles * BM * BN;
+  const size_t tbase = ((size_t)mt * ntiles + nt) * BM * BN;
   if (splits > 1) {
-    const size_t tstride = (size_t)mtiles * ntiles * BM * BN;
-    const size_t tbase = ((size_t)mt * ntiles + nt) * BM * BN;
     float *mine = g.part + (size_t)sp * tstride + tbase;
-    for (int e = threadIdx.x; e < BM * BN; e += NT)
-      __hip_atomic_store(mine + e, fin[(e / BN) * kTileFinStride + e % BN], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();
+      acc_to_fin(h);
+      __syncthreads();
+      for (int e = threadIdx.x; e < HM * BN; e += NT)
+        __hip_atomic_store(mine + h * HM * BN + e, fin[(e / BN) * kTileFinStride + e % BN], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
     __syncthreads();
     unsigned *ctr = g.counters + (size_t)mt * ntiles + nt;
     if (threadIdx.x == 0) s_flag = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (s_flag != (unsigned)(splits - 1)) return;  // another split finishes this tile
-    for (int e = threadIdx.x; e < BM * BN; e += NT) {
-      const float *src = g.part + tbase + e;
-      float sum = 0.f;
-      for (int q0 = 0; q0 < splits; q0 += 4) {  // loads of 4 splits in flight, summed in split order
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          v[u] = q0 + u < splits ? __hip_atomic_load(src + (size_t)(q0 + u) * tstride, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT)
-                                 : 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (q0 + u < splits) sum += v[u];
-      }
-      fin[(e / BN) * kTileFinStride + e % BN] = sum;
-    }
     if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
   }
-  if constexpr (E == GemmEpi::kStore || E == GemmEpi::kResidAdd) {
-    for (int e = threadIdx.x; e < BM * BN; e += NT) {
-      const int row = e / BN, col = e % BN;
-      const int m = m0 + row, n = n0 + col;
-      float v = fin[row * kTileFinStride + col];
-      if (m < g.M && n < g.N) {
-        const size_t o = (size_t)m * g.N + n;
-        if (E == GemmEpi::kResidAdd) v += g.out[o];
-        g.out[o] = v;
-      } else {
-        v = 0.f;
+  for (int h = 0; h < 2; ++h) {
+    const int mh = m0 + h * HM;  // first output row of this half
+    __syncthreads();             // the previous half's epilogue is done with the LDS tile
+    if (splits > 1) {
+      for (int e = threadIdx.x; e < HM * BN; e += NT) {
+        const float *src = g.part + tbase + h * HM * BN + e;
+        float sum = 0.f;
+        for (int q0 = 0; q0 < splits; q0 += 4) {  // loads of 4 splits in flight, summed in split order
+          float v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            v[u] = q0 + u < splits ? __hip_atomic_load(src + (size_t)(q0 + u) * tstride, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0.f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (q0 + u < splits) sum += v[u];
+        }
+        fin[(e / BN) * kTileFinStride + e % BN] = sum;
       }
-      fin[row * kTileFinStride + col] = v * v;
+    } else {
+      acc_to_fin(h);
     }
-    if (g.ss_out) {  // per-row sum of squares over this column tile, for norm on load
-      __syncthreads();
-      const int row = threadIdx.x >> 1, sub = threadIdx.x & 1;
-      float sq = 0.f;
-      for (int c = sub; c < BN; c += 2) sq += fin[row * kTileFinStride + c];
-      sq += __shfl_xor(sq, 1, 64);
-      if (sub == 0 && m0 + row < g.M) g.ss_out[(size_t)nt * g.M + m0 + row] = sq;
-    }
-  } else if constexpr (E == GemmEpi::kSwiGLU) {
-    for (int e = threadIdx.x; e < BM * OC; e += NT) {
-      const int row = e / OC, col = e % OC;
-      const int m = m0 + row, n = n0 + col;
-      if (m < g.M && n < g.N) {
-        const float gt = fin[row * kTileFinStride + col], up = fin[row * kTileFinStride + OC + col];
-        g.out[(size_t)m * g.N + n] = gt / (1.f + expf(-gt)) * up;
+    __syncthreads();
+    if (mh >= g.M) break;  // rows past M: nothing to store (uniform)
+    if constexpr (E == GemmEpi::kStore || E == GemmEpi::kResidAdd) {
+      for (int e = threadIdx.x; e < HM * BN; e += NT) {
+        const int row = e / BN, col = e % BN;
+        const int m = mh + row, n = n0 + col;
+        float v = fin[row * kTileFinStride + col];
+        if (m < g.M && n < g.N) {
+          const size_t o = (size_t)m * g.N + n;
+          if (E == GemmEpi::kResidAdd) v += g.out[o];
+          g.out[o] = v;
+        } else {
+          v = 0.f;
+        }
+        fin[row * kTileFinStride + col] = v * v;
       }
-    }
-  } else if constexpr (E == GemmEpi::kArgmax) {
-    const int row = threadIdx.x >> 1, sub = threadIdx.x & 1;
-    float best = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int c = sub; c < BN; c += 2)
-      if (n0 + c < g.N) argmax_merge(best, bi, fin[row * kTileFinStride + c], n0 + c);
-    const float ov = __shfl_xor(best, 1, 64);
-    const int oi = __shfl_xor(bi, 1, 64);
-    argmax_merge(best, bi, ov, oi);
-    if (sub == 0 && m0 + row < g.M) {
-      g.amax_val[(size_t)(m0 + row) * ntiles + nt] = best;
-      g.amax_idx[(size_t)(m0 + row) * ntiles + nt] = bi;
-    }
-  } else {  // head epilogues: BN / D heads per tile row, one (row, head) per wave at a time
-    const int D = g.head_dim, half = D / 2, hpt = BN / D;
-    const bool own = lane < half;
-    const int i1 = own ? lane : 0;
-    for (int q = wave; q < BM * hpt; q += NT / 64) {
-      const int row = q / hpt, hh = q % hpt, m = m0 + row;
-      if (m >= g.M) break;
-      if (n0 + hh * D >= g.N) continue;
-      head_epilogue<uint16_t, E>(g, n0 / D + hh, m, fin[row * kTileFinStride + hh * D + i1],
-                                 fin[row * kTileFinStride + hh * D + i1 + half], own, i1, D);
+      if (g.ss_out) {  // per-row sum of squares over this column tile, for norm on load
+        __syncthreads();
+        const int row = threadIdx.x >> 2, sub = threadIdx.x & 3;
+        float sq = 0.f;
+        for (int c = sub; c < BN; c += 4) sq += fin[row * kTileFinStride + c];
+        sq += __shfl_xor(sq, 1, 64);
+        sq += __shfl_xor(sq, 2, 64);
+        if (sub == 0 && mh + row < g.M) g.ss_out[(size_t)nt * g.M + mh + row] = sq;
+      }
+    } else if constexpr (E == GemmEpi::kSwiGLU) {
+      for (int e = threadIdx.x; e < HM * OC; e += NT) {
+        const int row = e / OC, col = e % OC;
+        const int m = mh + row, n = n0 + col;
+        if (m < g.M && n < g.N) {
+          const float gt = fin[row * kTileFinStride + col], up = fin[row * kTileFinStride + OC + col];
+          g.out[(size_t)m * g.N + n] = gt / (1.f + expf(-gt)) * up;
+        }
+      }
+    } else if constexpr (E == GemmEpi::kArgmax) {
+      const int row = threadIdx.x >> 2, sub = threadIdx.x & 3;
+      float best = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int c = sub; c < BN; c += 4)
+        if (n0 + c < g.N) argmax_merge(best, bi, fin[row * kTileFinStride + c], n0 + c);
+#pragma unroll
+      for (int o = 1; o <= 2; o <<= 1) {
+        const float ov = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        argmax_merge(best, bi, ov, oi);
+      }
+      if (sub == 0 && mh + row < g.M) {
+        g.amax_val[(size_t)(mh + row) * ntiles + nt] = best;
+        g.amax_idx[(size_t)(mh + row) * ntiles + nt] = bi;
+      }
+    } else {  // head epilogues: BN / D heads per tile row, one (row, head) per wave at a time
+      const int D = g.head_dim, half = D / 2, hpt = BN / D;
+      const bool own = lane < half;
+      const int i1 = own ? lane : 0;
+      for (int q = wave; q < HM * hpt; q += NT / 64) {
+        const int row = q / hpt, hh = q % hpt, m = mh + row;
+        if (m >= g.M) break;
+        if (n0 + hh * D >= g.N) continue;
+        head_epilogue<uint16_t, E>(g, n0 / D + hh, m, fin[row * kTileFinStride + hh * D + i1],
+                                   fin[row * kTileFinStride + hh * D + i1 + half], own, i1, D);
+      }
     }
   }
 }
 
 size_t tiled_lds_bytes() {
-  const size_t pipe = (size_t)kTileW + 2 * kTileWBytes, fin = (size_t)kTileM * kTileFinStride * sizeof(float);
+  const size_t pipe = (size_t)kTileW + 2 * kTileWBytes, fin = (size_t)kTileM / 2 * kTileFinStride * sizeof(float);
   return pipe > fin ? pipe : fin;
 }
 
