@@ -92,7 +92,7 @@ constexpr int kInjectChunk = 4096;  // rows per injection pass
 // fp32 partial buffer of a GEMM (split-K only).
 size_t gemm_part_floats(const GemmPlan &p, int M, int N, GemmEpi e) {
   if (p.splits <= 1) return 0;
-  if (p.tiled) return (size_t)p.splits * p.row_blocks * p.col_groups * 128 * 128;  // whole 128 x 128 tiles
+  if (p.tiled) return (size_t)p.splits * p.row_blocks * p.col_groups * p.tile_m * p.tile_n;  // whole tiles
   return (size_t)p.splits * M * N * (e == GemmEpi::kSwiGLU ? 2 : 1);
 }
 int gemm_tiles(const GemmPlan &p) { return p.col_groups * p.row_blocks; }

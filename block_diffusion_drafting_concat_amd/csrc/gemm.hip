@@ -647,11 +647,19 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
 //      work-groups and the last split of a tile reduces. Work-group order puts every row tile
 //      (and split) of a column tile on one XCD, back to back, so the weight tile is read from
 //      HBM once per column tile.
-constexpr int kTileM = 128, kTileN = 128, kTileK = 32;
-constexpr int kTileABytes = 2 * kTileM * kTileK * 2;  // A hi + A lo of one step (16 KiB)
-constexpr int kTileWBytes = kTileN * kTileK * 2;      // W of one step (8 KiB)
-constexpr int kTileW = 2 * kTileABytes;               // W slots follow the two A buffers
-constexpr int kTileFinStride = kTileN + 4;            // floats per row of the epilogue tile
+constexpr int kTileK = 32;
+// LDS of a BM x BN tile (128 x 128, or 64 x 256): two A buffers (hi and lo planes), two W
+// buffers, and the epilogue's half tile (BM / 2 rows of BN + 4 floats) over them
+template <int BM, int BN> struct TileLds {
+  static constexpr int kABytes = 2 * BM * kTileK * 2;  // A hi + A lo of one step
+  static constexpr int kWBytes = BN * kTileK * 2;      // W of one step
+  static constexpr int kW = 2 * kABytes;               // W slots follow the two A buffers
+  static constexpr int kFinStride = BN + 4;            // floats per row of the epilogue tile
+  static constexpr size_t bytes() {
+    return (size_t)kW + 2 * kWBytes > (size_t)BM / 2 * kFinStride * 4 ? (size_t)kW + 2 * kWBytes
+                                                                       : (size_t)BM / 2 * kFinStride * 4;
+  }
+};
 
 __device__ __forceinline__ int tile_swz(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
 
@@ -700,11 +708,16 @@ __global__ __launch_bounds__(256) void split_rows_kernel(GemmArgs g, uint16_t *_
 // kLo: A = the (hi, lo) planes from split_rows_kernel (g.a[0], g.a[1], row stride K), two
 // MFMAs per step. Otherwise A is bf16 as given (the auxiliary target states): g.a_nseg equal
 // K segments g.a[s] with row stride g.lda, each a multiple of the K step, one MFMA per step.
-template <GemmEpi E, bool kLo>
+template <GemmEpi E, bool kLo, int BM, int BN>
 __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int splits) {
-  constexpr int BM = kTileM, BN = kTileN, BK = kTileK, NT = 256;
+  constexpr int BK = kTileK, NT = 256;
+  constexpr int WM = BM / 2, WN = BN / 2;    // wave tile (2 x 2 waves)
+  constexpr int TF = WM / 16, UN = WN / 16;  // MFMA row and column tiles per wave
+  constexpr int JA = BM / 64, JW = BN / 64;  // 16-byte A (per plane) and W chunks per thread and K step
+  constexpr int FS = TileLds<BM, BN>::kFinStride, kTileABytes = TileLds<BM, BN>::kABytes;
+  constexpr int kTileW = TileLds<BM, BN>::kW, kTileWBytes = TileLds<BM, BN>::kWBytes;
   constexpr bool kDual = E == GemmEpi::kSwiGLU;
-  constexpr int OC = kDual ? BN / 2 : BN;  // output columns of a tile (SwiGLU: 64 gate + 64 up rows)
+  constexpr int OC = kDual ? BN / 2 : BN;  // output columns of a tile (SwiGLU: BN/2 gate + BN/2 up rows)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ unsigned s_flag;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
@@ -715,17 +728,18 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
   if (nt >= ntiles) return;
   const int m0 = mt * BM, n0 = nt * OC;
   const int K = g.K;
-  constexpr int NLD = kLo ? 3 : 2;  // 16-byte loads per chunk slot and K step: (hi, lo,) w
-  const int kseg = K / g.a_nseg;    // bf16 A: K columns per segment
-  // Loads of one K step, per thread: two 16-byte chunks of weight rows and two of activation
-  // rows (hi and lo each). Tile row r's chunk c is stored at tile_swz(r, c); thread slot
-  // (row 16 i + lane / 4, stored chunk lane % 4) holds source chunk (lane % 4) ^ swz(row).
-  const uint16_t *brow[2], *ahi[2], *alo[2];
-  size_t aoff[2];
-  int bsrc[2];
+  constexpr int NLD = (kLo ? 2 : 1) * JA + JW;  // 16-byte loads per thread and K step
+  const int kseg = K / g.a_nseg;                // bf16 A: K columns per segment
+  // Loads of one K step, per thread: JA 16-byte chunks of activation rows (hi and lo each)
+  // and JW of weight rows; chunk slot j of wave w is tile row (4 j + w) * 16 + lane / 4. Tile
+  // row r's chunk c is stored at tile_swz(r, c); thread slot (row, stored chunk lane % 4)
+  // holds source chunk (lane % 4) ^ swz(row).
+  const uint16_t *brow[JW], *ahi[JA], *alo[JA];
+  size_t aoff[JA];
+  int bsrc[JW], asrc[JA];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = (wave * 2 + j) * 16 + (lane >> 2);
+  for (int j = 0; j < JW; ++j) {
+    const int r = (j * 4 + wave) * 16 + (lane >> 2);
     // weight row of tile row r (a row past N reads a valid row; its results are never stored)
     const int n = min(n0 + (kDual ? (r & (OC - 1)) : r), g.N - 1);
     int seg = 0, nbase = 0;
@@ -733,6 +747,11 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
       while (seg < g.b_nseg - 1 && n >= g.b_end[seg]) nbase = g.b_end[seg++];
     brow[j] = reinterpret_cast<const uint16_t *>(kDual ? g.b[r < OC ? 0 : 1] : g.b[seg]) + (size_t)(n - nbase) * K;
     bsrc[j] = ((lane & 3) ^ ((r >> 2) & 3)) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < JA; ++j) {
+    const int r = (j * 4 + wave) * 16 + (lane >> 2);
+    asrc[j] = ((lane & 3) ^ ((r >> 2) & 3)) * 8;
     const int am = min(m0 + r, g.M - 1);  // rows past M: a valid row, never stored
     aoff[j] = (size_t)am * (kLo ? (size_t)K : (size_t)g.lda);
     ahi[j] = reinterpret_cast<const uint16_t *>(g.a[0]) + aoff[j];
@@ -742,40 +761,43 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
   // tiles are double buffered. Every iteration issues the same six loads (the K offset clamped
   // past the end), so a fixed count of loads stays in flight. (No LDS DMA here: after one the
   // compiler must assume every LDS read depends on it and waits for all loads in flight.)
-  Vec16 regs[2][3][2];  // [set][hi, lo, w][j]
+  Vec16 aregs[2][2][JA], wregs[2][JW];  // [set][hi, lo][j], [set][j]
   auto load = [&](int set, int k0) {
     if constexpr (!kLo) {  // the segment of the concatenated A holding columns [k0, k0 + BK)
       const int seg = k0 / kseg;
       const uint16_t *a0 = reinterpret_cast<const uint16_t *>(g.a[seg]) + (k0 - seg * kseg);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) regs[set][0][j] = load_vec16(a0 + aoff[j] + bsrc[j]);
+      for (int j = 0; j < JA; ++j) aregs[set][0][j] = load_vec16(a0 + aoff[j] + asrc[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < JA; ++j) {
+        aregs[set][0][j] = load_vec16(ahi[j] + k0 + asrc[j]);
+        aregs[set][1][j] = load_vec16(alo[j] + k0 + asrc[j]);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if constexpr (kLo) {
-        regs[set][0][j] = load_vec16(ahi[j] + k0 + bsrc[j]);
-        regs[set][1][j] = load_vec16(alo[j] + k0 + bsrc[j]);
-      }
-      regs[set][2][j] = load_vec16(brow[j] + k0 + bsrc[j]);
-    }
+    for (int j = 0; j < JW; ++j) wregs[set][j] = load_vec16(brow[j] + k0 + bsrc[j]);
   };
   auto store = [&](int set, int buf) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int o = (wave * 2 + j) * 1024 + lane * 16;
-      *reinterpret_cast<uint4 *>(smem + buf * kTileABytes + o) = regs[set][0][j].u;
-      if constexpr (kLo) *reinterpret_cast<uint4 *>(smem + buf * kTileABytes + BM * BK * 2 + o) = regs[set][1][j].u;
-      *reinterpret_cast<uint4 *>(smem + kTileW + buf * kTileWBytes + o) = regs[set][2][j].u;
+    for (int j = 0; j < JA; ++j) {
+      const int o = (j * 4 + wave) * 1024 + lane * 16;
+      *reinterpret_cast<uint4 *>(smem + buf * kTileABytes + o) = aregs[set][0][j].u;
+      if constexpr (kLo) *reinterpret_cast<uint4 *>(smem + buf * kTileABytes + BM * BK * 2 + o) = aregs[set][1][j].u;
     }
+#pragma unroll
+    for (int j = 0; j < JW; ++j)
+      *reinterpret_cast<uint4 *>(smem + kTileW + buf * kTileWBytes + (j * 4 + wave) * 1024 + lane * 16) = wregs[set][j].u;
   };
-  // vmcnt(NLD * 2): the newest step's loads may stay in flight
-  constexpr unsigned kWaitOlder = 0x0F70u | (unsigned)(NLD * 2);
+  // vmcnt(NLD): the newest step's loads may stay in flight
+  static_assert(NLD <= 15, "vmcnt field");
+  constexpr unsigned kWaitOlder = 0x0F70u | (unsigned)NLD;
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[TF][UN];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < TF; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < UN; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // this split's K steps [ks0, ks0 + nk) of the K / BK (splits of near-equal length)
   const int ks0 = (int)((long)sp * (K / BK) / splits), nk = (int)((long)(sp + 1) * (K / BK) / splits) - ks0;
   auto kof = [&](int step) { return (ks0 + min(step, nk - 1)) * BK; };
@@ -791,17 +813,17 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
     load(set, kof(ks + 2));  // set ks % 2 held step ks, already in LDS
     const unsigned char *sa = smem + set * kTileABytes;
     const unsigned char *sw = smem + kTileW + set * kTileWBytes;
-    Vec16 bf[4];
+    Vec16 bf[UN];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) bf[u].u = *reinterpret_cast<const uint4 *>(sw + tile_swz(wn * 64 + u * 16 + (lane & 15), lane >> 4));
+    for (int u = 0; u < UN; ++u) bf[u].u = *reinterpret_cast<const uint4 *>(sw + tile_swz(wn * WN + u * 16 + (lane & 15), lane >> 4));
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int o = tile_swz(wm * 64 + t * 16 + (lane & 15), lane >> 4);
+    for (int t = 0; t < TF; ++t) {
+      const int o = tile_swz(wm * WM + t * 16 + (lane & 15), lane >> 4);
       Vec16 ah, al;
       ah.u = *reinterpret_cast<const uint4 *>(sa + o);
       if constexpr (kLo) al.u = *reinterpret_cast<const uint4 *>(sa + BM * BK * 2 + o);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < UN; ++u) {
         mma16<uint16_t>(acc[t][u], ah, bf[u]);
         if constexpr (kLo) mma16<uint16_t>(acc[t][u], al, bf[u]);
       }
@@ -822,16 +844,17 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
   //      so the epilogue needs half the LDS of the tile and three work-groups fit on a CU.
   //      MFMA layout: lane holds rows (lane / 16) * 4 + i, column lane % 16.
   constexpr int HM = BM / 2;
+  constexpr int TPR = NT / HM;  // threads per row of a half tile in the row-wise epilogues
   float *fin = reinterpret_cast<float *>(smem);
   auto acc_to_fin = [&](int h) {
     if (wm == h)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < TF; ++t)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < UN; ++u)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            fin[(t * 16 + (lane >> 4) * 4 + i) * kTileFinStride + wn * 64 + u * 16 + (lane & 15)] = acc[t][u][i];
+            fin[(t * 16 + (lane >> 4) * 4 + i) * FS + wn * WN + u * 16 + (lane & 15)] = acc[t][u][i];
   };
   // ---- split-K: every split stores its tile ([split][row tile][column tile] blocks of
   //      BM x BN in the workspace) and the last to arrive sums all splits in split order, with
@@ -846,7 +869,7 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
       acc_to_fin(h);
       __syncthreads();
       for (int e = threadIdx.x; e < HM * BN; e += NT)
-        __hip_atomic_store(mine + h * HM * BN + e, fin[(e / BN) * kTileFinStride + e % BN], __ATOMIC_RELAXED,
+        __hip_atomic_store(mine + h * HM * BN + e, fin[(e / BN) * FS + e % BN], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
@@ -875,7 +898,7 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
           for (int u = 0; u < 4; ++u)
             if (q0 + u < splits) sum += v[u];
         }
-        fin[(e / BN) * kTileFinStride + e % BN] = sum;
+        fin[(e / BN) * FS + e % BN] = sum;
       }
     } else {
       acc_to_fin(h);
@@ -886,7 +909,7 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
       for (int e = threadIdx.x; e < HM * BN; e += NT) {
         const int row = e / BN, col = e % BN;
         const int m = mh + row, n = n0 + col;
-        float v = fin[row * kTileFinStride + col];
+        float v = fin[row * FS + col];
         if (m < g.M && n < g.N) {
           const size_t o = (size_t)m * g.N + n;
           if (E == GemmEpi::kResidAdd) v += g.out[o];
@@ -894,15 +917,15 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
         } else {
           v = 0.f;
         }
-        fin[row * kTileFinStride + col] = v * v;
+        fin[row * FS + col] = v * v;
       }
       if (g.ss_out) {  // per-row sum of squares over this column tile, for norm on load
         __syncthreads();
-        const int row = threadIdx.x >> 2, sub = threadIdx.x & 3;
+        const int row = threadIdx.x / TPR, sub = threadIdx.x % TPR;
         float sq = 0.f;
-        for (int c = sub; c < BN; c += 4) sq += fin[row * kTileFinStride + c];
-        sq += __shfl_xor(sq, 1, 64);
-        sq += __shfl_xor(sq, 2, 64);
+        for (int c = sub; c < BN; c += TPR) sq += fin[row * FS + c];
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) sq += __shfl_xor(sq, o, 64);
         if (sub == 0 && mh + row < g.M) g.ss_out[(size_t)nt * g.M + mh + row] = sq;
       }
     } else if constexpr (E == GemmEpi::kSwiGLU) {
@@ -910,18 +933,18 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
         const int row = e / OC, col = e % OC;
         const int m = mh + row, n = n0 + col;
         if (m < g.M && n < g.N) {
-          const float gt = fin[row * kTileFinStride + col], up = fin[row * kTileFinStride + OC + col];
+          const float gt = fin[row * FS + col], up = fin[row * FS + OC + col];
           g.out[(size_t)m * g.N + n] = gt / (1.f + expf(-gt)) * up;
         }
       }
     } else if constexpr (E == GemmEpi::kArgmax) {
-      const int row = threadIdx.x >> 2, sub = threadIdx.x & 3;
+      const int row = threadIdx.x / TPR, sub = threadIdx.x % TPR;
       float best = -INFINITY;
       int bi = 0x7fffffff;
-      for (int c = sub; c < BN; c += 4)
-        if (n0 + c < g.N) argmax_merge(best, bi, fin[row * kTileFinStride + c], n0 + c);
+      for (int c = sub; c < BN; c += TPR)
+        if (n0 + c < g.N) argmax_merge(best, bi, fin[row * FS + c], n0 + c);
 #pragma unroll
-      for (int o = 1; o <= 2; o <<= 1) {
+      for (int o = 1; o < TPR; o <<= 1) {
         const float ov = __shfl_xor(best, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
         argmax_merge(best, bi, ov, oi);
@@ -938,21 +961,16 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
         const int row = q / hpt, hh = q % hpt, m = mh + row;
         if (m >= g.M) break;
         if (n0 + hh * D >= g.N) continue;
-        head_epilogue<uint16_t, E>(g, n0 / D + hh, m, fin[row * kTileFinStride + hh * D + i1],
-                                   fin[row * kTileFinStride + hh * D + i1 + half], own, i1, D);
+        head_epilogue<uint16_t, E>(g, n0 / D + hh, m, fin[row * FS + hh * D + i1],
+                                   fin[row * FS + hh * D + i1 + half], own, i1, D);
       }
     }
   }
 }
 
-size_t tiled_lds_bytes() {
-  const size_t pipe = (size_t)kTileW + 2 * kTileWBytes, fin = (size_t)kTileM / 2 * kTileFinStride * sizeof(float);
-  return pipe > fin ? pipe : fin;
-}
-
-template <GemmEpi E, bool kLo>
-hipError_t launch_tiled(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
-  auto kern = gemm_tiled_kernel<E, kLo>;
+template <GemmEpi E, bool kLo, int BM, int BN>
+hipError_t launch_tiled_shape(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
+  auto kern = gemm_tiled_kernel<E, kLo, BM, BN>;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           kMaxLds - 1024);
@@ -966,8 +984,14 @@ hipError_t launch_tiled(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
     t.a[1] = lo;
     t.a_nseg = 1;
   }
-  kern<<<(ntiles + 7) / 8 * 8 * mtiles * p.splits, 256, tiled_lds_bytes(), s>>>(t, mtiles, ntiles, p.splits);
+  kern<<<(ntiles + 7) / 8 * 8 * mtiles * p.splits, 256, TileLds<BM, BN>::bytes(), s>>>(t, mtiles, ntiles,
+                                                                                         p.splits);
   return hipGetLastError();
+}
+
+template <GemmEpi E, bool kLo>
+hipError_t launch_tiled(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
+  return p.tile_n == 256 ? launch_tiled_shape<E, kLo, 64, 256>(g, p, s) : launch_tiled_shape<E, kLo, 128, 128>(g, p, s);
 }
 
 template <typename T, int MT, int CW, int CT, int KW, GemmEpi E, bool kAF32>
@@ -1088,8 +1112,16 @@ GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bo
       head_fits) {
     p.tiled = 1;
     p.cw = 8, p.ct = 1, p.kw = 1;
-    p.col_groups = epi == GemmEpi::kSwiGLU ? (N + kTileN / 2 - 1) / (kTileN / 2) : (N + kTileN - 1) / kTileN;
-    p.row_blocks = (M + kTileM - 1) / kTileM;
+    // Every column tile rereads all of A, while the row tiles of a column tile run back to
+    // back on one XCD and share its weight tile through that XCD's L2 (4 MiB) when it fits.
+    // 64 x 256 tiles halve the A rereads (the dominant traffic at batch 128: the LM head's A
+    // is 19 MB, read once per column tile), as long as a 256-row weight tile (256 K bf16)
+    // still fits the L2; longer K (fc over the concatenated states, the down projection)
+    // keeps 128 x 128 tiles.
+    p.tile_n = (long)256 * K * 2 <= (4L << 20) ? 256 : 128;
+    p.tile_m = p.tile_n == 256 ? 64 : 128;
+    p.col_groups = epi == GemmEpi::kSwiGLU ? (N + p.tile_n / 2 - 1) / (p.tile_n / 2) : (N + p.tile_n - 1) / p.tile_n;
+    p.row_blocks = (M + p.tile_m - 1) / p.tile_m;
     // Split-K when there are fewer tiles than CUs: the split count minimising the rounds (of
     // one work-group per CU: a second one on a CU shares its LDS and matrix cores and adds
     // little) per unit of work, plus a small cost per extra split for the reduction through
@@ -1152,14 +1184,15 @@ GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bo
 hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, const GemmPlan &p, hipStream_t s) {
   ProfScope prof(g0.tag ? g0.tag : "gemm", s);
   if (p.tiled) {
-    const int oc = epi == GemmEpi::kSwiGLU ? kTileN / 2 : kTileN;
+    const int oc = epi == GemmEpi::kSwiGLU ? p.tile_n / 2 : p.tile_n;
     const bool head = epi == GemmEpi::kHeadNormRope || epi == GemmEpi::kKvScatter;
     const bool a_ok = g0.a_f32 ? g0.a_nseg == 1 && g0.a_split && (!(g0.norm_w || g0.a_out) || g0.ss)
                                : epi == GemmEpi::kStore && g0.a_nseg >= 1 && g0.a_nseg <= 8 &&
                                      g0.K % g0.a_nseg == 0 && (g0.K / g0.a_nseg) % kTileK == 0 && !g0.norm_w &&
                                      !g0.a_out && g0.keep_bs == 0 && g0.lda % 8 == 0;
     if (!bf16 || !a_ok || g0.K % kTileK || g0.M < 1 || g0.keep_bs == 1 || p.col_groups != (g0.N + oc - 1) / oc ||
-        p.row_blocks != (g0.M + kTileM - 1) / kTileM || g0.b_nseg < 1 || g0.b_nseg > 3 || p.splits < 1 ||
+        p.row_blocks != (g0.M + p.tile_m - 1) / p.tile_m || !((p.tile_m == 128 && p.tile_n == 128) ||
+        (p.tile_m == 64 && p.tile_n == 256)) || g0.b_nseg < 1 || g0.b_nseg > 3 || p.splits < 1 ||
         p.splits > g0.K / kTileK || (p.splits > 1 && (!g0.part || !g0.counters)) ||
         (head && ((g0.head_dim != 64 && g0.head_dim != 128) || g0.N % g0.head_dim)))
       return hipErrorInvalidValue;

@@ -98,7 +98,8 @@ struct GemmPlan {
   int grid_x;
   int lds_budget;
   int col_groups, row_blocks;  // output tiles = col_groups * row_blocks (split-K counters)
-  int tiled;                   // 1: the LDS-tiled kernel for many rows (128 x 128 output tiles)
+  int tiled;                   // 1: the LDS-tiled kernel for many rows (tile_m x tile_n output tiles)
+  int tile_m, tile_n;          // tiled: 128 x 128 or 64 x 256
 };
 // a_f32: the activations are fp32 rows (else the storage type, as the auxiliary target states,
 // in a_segs equal K segments)
