@@ -42,15 +42,17 @@ GEMM_KERNELS = {
     "gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=2,NCG=1,kStore,multi-A>": ("gemm.fc",),
     "gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=1,NCG=1,kKvScatter,fp32-A>": ("gemm.kv",),
 }
-# More than 64 rows (batch 32 and 128): the LDS-tiled kernel, one instance per epilogue
-# (fc reads the auxiliary states as bf16, every other projection fp32 activations as hi + lo).
+# More than 64 rows (batch 32 and 128): the LDS-tiled kernel, one instance per epilogue and
+# tile shape (fc reads the auxiliary states as bf16, every other projection fp32 activations
+# as hi + lo). O and down share an instance, so the tiled kernels are reported per projection.
 TILED_KERNELS = {
-    "gemm_tiled_kernel<kHeadNormRope,hi+lo-A>": ("gemm.qkv",),
-    "gemm_tiled_kernel<kResidAdd,hi+lo-A>": ("gemm.o", "gemm.down"),
-    "gemm_tiled_kernel<kSwiGLU,hi+lo-A>": ("gemm.gate_up",),
-    "gemm_tiled_kernel<kArgmax,hi+lo-A>": ("gemm.lm_head",),
-    "gemm_tiled_kernel<kStore,bf16-A>": ("gemm.fc",),
-    "gemm_tiled_kernel<kKvScatter,hi+lo-A>": ("gemm.kv",),
+    "gemm_tiled_kernel<kHeadNormRope,hi+lo-A> (qkv)": ("gemm.qkv",),
+    "gemm_tiled_kernel<kResidAdd,hi+lo-A> (o)": ("gemm.o",),
+    "gemm_tiled_kernel<kResidAdd,hi+lo-A> (down)": ("gemm.down",),
+    "gemm_tiled_kernel<kSwiGLU,hi+lo-A> (gate_up)": ("gemm.gate_up",),
+    "gemm_tiled_kernel<kArgmax,hi+lo-A> (lm_head)": ("gemm.lm_head",),
+    "gemm_tiled_kernel<kStore,bf16-A> (fc)": ("gemm.fc",),
+    "gemm_tiled_kernel<kKvScatter,hi+lo-A> (kv)": ("gemm.kv",),
 }
 GEMM_SOURCES = ("block_diffusion_drafting_concat_amd/csrc/gemm.hip", "block_diffusion_drafting_concat_amd/csrc/common.h")
 
@@ -375,6 +377,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    # the faster of the two ways of running the same step: replays of the captured graph, or
+    # eager launches with no event (both enqueue the identical kernels)
+    sec_best, timing = sec_plain, "eager launches (no events)"
+    if sec_graph and sec_graph <= sec_plain:
+        sec_best, timing = sec_graph, "replays of the captured step graph"
     st = bench.stats.cpu().numpy().astype(float)
     acceptance = {"num_drafts": int(st[0]), "num_draft_tokens": int(st[1]), "num_accepted_tokens": int(st[2]),
                   "rate": st[2] / st[1] if st[1] else None, "length": 1 + st[2] / st[0] if st[0] else None,
@@ -401,12 +408,12 @@ def main():
     sbytes = step_bytes(spec, B, bench.ctx, wl.inject_rows)
     result = {
         "metric": "drafted tokens/sec and draft blocks/sec (Qwen3-8B-shape, b16); % HBM/MFMA roofline",
-        "value": B * K / (sec_graph if sec_graph else sec),
+        "value": B * K / sec_best,
         "unit": "drafted tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": (sec_graph if sec_graph else sec) * 1e3,
+        "ms_per_step": sec_best * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -417,15 +424,16 @@ def main():
                    "hidden": spec.hidden, "layers": spec.n_layers, "heads": [spec.n_q_heads, spec.n_kv_heads],
                    "head_dim": spec.head_dim, "intermediate": spec.intermediate, "vocab": spec.vocab,
                    "fc_in": spec.n_aux * spec.target_hidden, "page_size": wl.page_size},
-        "draft_blocks_per_s": B / (sec_graph if sec_graph else sec),
-        "timing": "replays of the captured step graph" if sec_graph else "eager launches",
+        "draft_blocks_per_s": B / sec_best,
+        "timing": timing,
+        "ms_per_step_graph": sec_graph * 1e3 if sec_graph else None,
         "ms_per_step_eager": sec * 1e3,
         "acceptance": acceptance,
         "ms_per_step_without_events": sec_plain * 1e3,
         "launches_per_step": sum(v[0] for v in prof_all.values()) / n_prof,
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": sbytes,
-                          "achieved": sbytes / (sec_graph if sec_graph else sec) / 1e9, "peak": HBM_PEAK_GBS,
-                          "unit": "GB/s", "frac": sbytes / (sec_graph if sec_graph else sec) / 1e9 / HBM_PEAK_GBS},
+                          "achieved": sbytes / sec_best / 1e9, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": sbytes / sec_best / 1e9 / HBM_PEAK_GBS},
         "roofline": roofline,
         "kernel_ms_per_step_all_events": {k: v[1] / n_prof for k, v in sorted(prof_all.items())},
         "gemm_kernels_all_events": {k: {"launches_per_step": v[0] / n_prof, "ms_per_step": v[1] / n_prof,

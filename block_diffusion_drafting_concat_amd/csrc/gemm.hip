@@ -1118,7 +1118,14 @@ GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bo
     // is 19 MB, read once per column tile), as long as a 256-row weight tile (256 K bf16)
     // still fits the L2; longer K (fc over the concatenated states, the down projection)
     // keeps 128 x 128 tiles.
-    p.tile_n = (long)256 * K * 2 <= (4L << 20) ? 256 : 128;
+    // With up to 4 K splits a 256-row weight tile of one split fits (the down projection):
+    // the splits' partials cost far less than the A rereads. (fc, whose bf16 input is half
+    // the bytes, measured faster unsplit with 128 x 128 tiles.)
+    int smin = 1;
+    while (a_f32 && (long)256 * (K / smin) * 2 > (4L << 20) && smin < 4) ++smin;
+    const bool wide = (long)256 * (K / smin) * 2 <= (4L << 20) && K / kTileK >= 32 * smin;
+    p.tile_n = wide ? 256 : 128;
+    if (!wide) smin = 1;
     p.tile_m = p.tile_n == 256 ? 64 : 128;
     p.col_groups = epi == GemmEpi::kSwiGLU ? (N + p.tile_n / 2 - 1) / (p.tile_n / 2) : (N + p.tile_n - 1) / p.tile_n;
     p.row_blocks = (M + p.tile_m - 1) / p.tile_m;
@@ -1127,8 +1134,8 @@ GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bo
     // little) per unit of work, plus a small cost per extra split for the reduction through
     // the workspace; at least 32 K steps per split.
     const long wgs = (long)p.col_groups * p.row_blocks, slots = cu_count();
-    p.splits = 1;
-    if (wgs < slots) {
+    p.splits = smin;
+    if (smin == 1 && wgs < slots) {
       double best = 1.0;
       for (int s = 2; s <= 8 && 32 * s <= K / kTileK; ++s) {
         const double cost = (double)((wgs * s + slots - 1) / slots) / s + 0.03 * (s - 1);

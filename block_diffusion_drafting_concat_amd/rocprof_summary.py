@@ -45,9 +45,10 @@ def short_name(name: str) -> str:
              f"NCG={m.group(6)},{EPI[m.group(7)]}")
         s += ",multi-A" if m.group(8) == "true" else ""
         return s + (",fp32-A>" if m.group(9) == "true" else ">")
-    m = re.search(r"gemm_tiled_kernel<\(dflash::GemmEpi\)(\d), (true|false)>", name)
+    m = re.search(r"gemm_tiled_kernel<\(dflash::GemmEpi\)(\d), (true|false), (\d+), (\d+)>", name)
     if m:
-        return f"gemm_tiled_kernel<{EPI[m.group(1)]},{'hi+lo-A' if m.group(2) == 'true' else 'bf16-A'}>"
+        return (f"gemm_tiled_kernel<{EPI[m.group(1)]},{'hi+lo-A' if m.group(2) == 'true' else 'bf16-A'},"
+                f"{m.group(3)}x{m.group(4)}>")
     name = re.sub(r"^void ", "", name)
     name = name.replace("dflash::(anonymous namespace)::", "")
     return re.sub(r"\(.*$", "", name)
