@@ -400,9 +400,10 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 }  // namespace
 
 void attn_plan(int B, int KVH, int max_keys, int *chunk, int *nsplit) {
-  // Aim for ~1024 work-groups in total, in splits of at least one 64-key tile and at most
-  // eight: with many sequences of unequal length, short splits keep the work-groups even.
-  long want = (long)max_keys * B * KVH / 1024;
+  // Aim for ~768 work-groups in total (one round at three per CU), in splits of at least one
+  // 64-key tile and at most eight: with many sequences of unequal length, short splits keep
+  // the work-groups even.
+  long want = (long)max_keys * B * KVH / 768;
   int ch = (int)((want + kTileKeys - 1) / kTileKeys) * kTileKeys;
   if (ch < kTileKeys) ch = kTileKeys;
   if (ch > 8 * kTileKeys) ch = 8 * kTileKeys;
