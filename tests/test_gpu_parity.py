@@ -13,6 +13,11 @@ SMALL_BF16 = synth.DrafterSpec(hidden=256, n_layers=2, n_q_heads=8, n_kv_heads=2
                                intermediate=512, vocab=2048, n_aux=2, target_hidden=192, block_size=16,
                                mask_token_id=2047, rope_theta=1e6, dtype="bf16")
 TINY = synth.WORKLOADS["tiny_fp32_b1"].spec
+# a long down projection (K = 3200: 100 K steps): with more than 64 rows its few tiles split K
+# three ways over work-groups, in uneven ranges (33, 33, 34 steps)
+SMALL_BF16_LONG_MLP = synth.DrafterSpec(hidden=256, n_layers=1, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                        intermediate=3200, vocab=2048, n_aux=2, target_hidden=192,
+                                        block_size=16, mask_token_id=2047, rope_theta=1e6, dtype="bf16")
 # head_dim 64 (two heads per 128-column tile of the tiled GEMM), four auxiliary segments of
 # 96 columns (three K steps each), a ragged vocabulary tile (1008)
 SMALL_BF16_D64 = synth.DrafterSpec(hidden=384, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64,
@@ -55,6 +60,7 @@ def _compare_cache(spec, st, kc, vc, seqs):
     (SMALL_BF16_D64, [70, 3, 150, 0, 33, 90, 12, 20, 64, 100], 16, True),
     # every sequence within one 64-key attention split: normalised in place, no merge launch
     (SMALL_BF16, [0, 20, 3, 40], 16, True),
+    (SMALL_BF16_LONG_MLP, [5, 90, 0, 33, 70], 16, True),
 ])
 def test_inject_and_propose_match_oracle(spec, ctx, P, shuffle):
     print(f"\n[case] spec={spec.dtype} H={spec.hidden} ctx={ctx} P={P}", flush=True)
