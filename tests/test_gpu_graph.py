@@ -18,7 +18,9 @@ SPEC = synth.DrafterSpec(hidden=256, n_layers=2, n_q_heads=8, n_kv_heads=2, head
 
 
 @pytest.mark.parametrize("ctx,acc", [([300, 77, 150], [1, SPEC.block_size, 6]),
-                                     ([300], [6])])  # one sequence: the chained post-attention block
+                                     ([300], [6]),  # one sequence: one row tile per projection
+                                     # 96 block rows: the tiled GEMM, its split-K counters
+                                     ([300, 77, 150, 40, 200, 90], [1, SPEC.block_size, 6, 3, 9, 2])])
 def test_captured_step_replays_match_the_eager_step(ctx, acc):
     ctx = np.array(ctx, np.int32)
     st = Setup(SPEC, ctx, seed=3)
