@@ -633,20 +633,20 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
 }
 
 
-// ---- Many rows (M > 64): LDS-tiled MFMA GEMM. A work-group computes a 128 x 128 tile of
-//      C = A W^T with 4 waves (2 x 2, 64 x 64 each, 4 x 4 MFMA tiles) and walks K in steps of
-//      32. A first pass (split_rows_kernel) normalises the fp32 activation rows (norm on
-//      load) and splits them into the exact (hi, lo) pair of bf16 planes once, not once per
-//      column tile; the weight and activation tiles then go through registers into LDS, the
-//      loads of two steps in flight while a step's 32 MFMAs per wave run. The LDS tiles are
-//      [128 rows][32] bf16 with the 16-byte chunks of a row XOR-swizzled by (row / 4) % 4, so
-//      the 16 rows of a fragment read fall on distinct banks. The tile then goes through LDS to
-//      the epilogue in two halves of 64 rows (fp32 store / residual add with per-tile row sums
-//      of squares, SwiGLU, per-tile argmax, the head epilogues), which keeps a work-group at
-//      48 KiB of LDS: three fit on a CU. With fewer tiles than CUs, K is split over
-//      work-groups and the last split of a tile reduces. Work-group order puts every row tile
-//      (and split) of a column tile on one XCD, back to back, so the weight tile is read from
-//      HBM once per column tile.
+// ---- Many rows (M > 64): LDS-tiled MFMA GEMM. A work-group computes a BM x BN tile of
+//      C = A W^T (128 x 128 with 64 x 64 per wave, or 64 x 256 with 32 x 128 per wave; 2 x 2
+//      waves) and walks K in steps of 32. A first pass (split_rows_kernel) normalises the
+//      fp32 activation rows (norm on load) and splits them into the exact (hi, lo) pair of
+//      bf16 planes once, not once per column tile; the weight and activation tiles then go
+//      through registers into LDS, the loads of two steps in flight while a step's MFMAs run.
+//      The LDS tiles are [rows][32] bf16 with the 16-byte chunks of a row XOR-swizzled by
+//      (row / 4) % 4, so the 16 rows of a fragment read fall on distinct banks. The tile then
+//      goes through LDS to the epilogue in two halves (fp32 store / residual add with per-tile
+//      row sums of squares, SwiGLU, per-tile argmax, the head epilogues), which keeps a
+//      work-group at 48 KiB of LDS: three fit on a CU. With fewer tiles than CUs, or to keep a
+//      wide weight tile within one XCD's L2, K is split over work-groups and the last split of
+//      a tile reduces. Work-group order puts every row tile (and split) of a column tile on one
+//      XCD, back to back, so the weight tile is read from HBM once per column tile.
 constexpr int kTileK = 32;
 // LDS of a BM x BN tile (128 x 128, or 64 x 256): two A buffers (hi and lo planes), two W
 // buffers, and the epilogue's half tile (BM / 2 rows of BN + 4 floats) over them
