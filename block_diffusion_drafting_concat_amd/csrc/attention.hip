@@ -274,9 +274,39 @@ __global__ __launch_bounds__(256, 3) void attn_partial_kernel(AttnArgs a) {
   }
 }
 
+// Online log-sum-exp accumulation of up to 16 split partials (m, l, o) into a running
+// (m_acc, l_acc, o_acc) of one output element, in split order: the loads of all 16 are issued
+// before any is used, so one round trip covers 16 splits.
+__device__ __forceinline__ void merge16(const float *pm, const float *pl, const float *po, size_t stride_ml,
+                                        size_t stride_o, int s0, int step, int ns, float &m_acc, float &l_acc,
+                                        float &o_acc) {
+  float mv[16], lv[16], pv[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int q = min(s0 + u * step, ns - 1);
+    mv[u] = pm[(size_t)q * stride_ml];
+    lv[u] = pl[(size_t)q * stride_ml];
+    pv[u] = po[(size_t)q * stride_o];
+  }
+  float m_new = m_acc;
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (s0 + u * step < ns) m_new = fmaxf(m_new, mv[u]);
+  const float r = exp2f(m_acc - m_new);  // m_acc = -inf at first: r = 0 on empty sums
+  l_acc *= r;
+  o_acc *= r;
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (s0 + u * step < ns) {
+      const float w = exp2f(mv[u] - m_new);
+      l_acc += w * lv[u];
+      o_acc += w * pv[u];
+    }
+  m_acc = m_new;
+}
+
 // Merge of up to 16 splits per sequence: thread (query row, d) of a (sequence, kv head),
-// 256 / D rows per work-group. The split weights are exp2(m_s - max m); the loads of 16 splits are in flight
-// together, and the sums run in split order.
+// 256 / D rows per work-group, one round trip for all splits.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int D = a.D, rpw = 256 / D;
@@ -288,47 +318,19 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
   if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel
   const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64 + row;
-  const float *pm = a.pm + base, *pl = a.pl + base, *po = a.po + base * D + d;
-  float mmax = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += 16) {
-    float mv[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) mv[u] = pm[(size_t)min(s0 + u, ns - 1) * 64];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) mmax = fmaxf(mmax, mv[u]);
-  }
-  float num = 0.f, den = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 16) {
-    float pv[16], mv[16], lv[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const size_t q = (size_t)min(s0 + u, ns - 1) * 64;
-      pv[u] = po[q * D];
-      mv[u] = pm[q];
-      lv[u] = pl[q];
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (s0 + u < ns) {
-        const float w = exp2f(mv[u] - mmax);
-        num += w * pv[u];
-        den += w * lv[u];
-      }
-  }
+  float m = -INFINITY, l = 0.f, o = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 16) merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, 1, ns, m, l, o);
   const int hh = row / a.bs, j = row % a.bs;
-  a.o[((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d] = num / den;
+  a.o[((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d] = o / l;
 }
 
 // Merge of many splits (more than 16 per sequence: one long context): work-group = one
-// (sequence, kv head, query row). Thread (d, sub) sums the splits s = sub (mod 256 / D) for
-// element d with the split weights exp2(m_s - max m); the
-// loads of 16 splits are issued together, and the sub-sums are combined through LDS in a
-// fixed order.
+// (sequence, kv head, query row). Thread (d, sub) accumulates the splits s = sub (mod 256 / D)
+// for element d, 16 loads in flight at a time; the sub-accumulators are then combined through
+// LDS in a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge_rows_kernel(AttnArgs a) {
-  __shared__ float red[4];
-  __shared__ float rnum[256];
-  __shared__ float rden[4];
+  __shared__ float sm[4], sl[4], so[256];
   const int row = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.QH / a.KVH;
   const int D = a.D, nsub = 256 / D;
@@ -337,37 +339,23 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(AttnArgs a) {
   const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
   if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel
   const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64 + row;
-  float mloc = -INFINITY;
-  for (int s = threadIdx.x; s < ns; s += 256) mloc = fmaxf(mloc, a.pm[base + (size_t)s * 64]);
-  mloc = wave_max(mloc);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mloc;
-  __syncthreads();
-  const float mmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float num = 0.f, den = 0.f;
-  for (int s0 = sub; s0 < ns; s0 += 16 * nsub) {
-    float pv[16], mv[16], lv[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int s = min(s0 + u * nsub, ns - 1);
-      pv[u] = a.po[(base + (size_t)s * 64) * D + d];
-      mv[u] = a.pm[base + (size_t)s * 64];
-      lv[u] = a.pl[base + (size_t)s * 64];
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const float w = s0 + u * nsub < ns ? exp2f(mv[u] - mmax) : 0.f;
-      num += w * pv[u];
-      den += w * lv[u];
-    }
+  float m = -INFINITY, l = 0.f, o = 0.f;
+  for (int s0 = sub; s0 < ns; s0 += 16 * nsub)
+    merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, nsub, ns, m, l, o);
+  so[threadIdx.x] = o;
+  if (d == 0) {
+    sm[sub] = m;
+    sl[sub] = l;
   }
-  rnum[threadIdx.x] = num;
-  if (d == 0) rden[sub] = den;
   __syncthreads();
   if (sub == 0) {
+    float mm = -INFINITY;
+    for (int q = 0; q < nsub; ++q) mm = fmaxf(mm, sm[q]);
     float n = 0.f, dn = 0.f;
     for (int q = 0; q < nsub; ++q) {
-      n += rnum[q * D + d];
-      dn += rden[q];
+      const float w = exp2f(sm[q] - mm);  // a sub with no split: m = -inf, weight 0
+      n += w * so[q * D + d];
+      dn += w * sl[q];
     }
     const int hh = row / a.bs, j = row % a.bs;
     a.o[((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d] = n / dn;
