@@ -57,5 +57,39 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-only AddressSanitizer: every -fsanitize flag goes to the host compilation (-Xarch_host),
+# so the GPU code objects are built as usual.
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_DRIVER = os.path.join(BUILD, "abi_asan")
+
+
+def build_asan_driver() -> str:
+    """Build the host ABI checks (tests/abi_asan_main.cpp) against api.cpp and profile.cpp
+    compiled with host-only AddressSanitizer and the regular kernel objects. Returns the path
+    of the executable."""
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    kern = [os.path.join(BUILD, n) for n in ("gemm.o", "attention.o", "rowwise.o")]
+    if not all(os.path.exists(k) for k in kern):
+        build()
+    srcs = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "profile.cpp"),
+            os.path.join(ROOT, "tests", "abi_asan_main.cpp")]
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(BUILD, "asan_" + os.path.splitext(os.path.basename(src))[0] + ".o")
+        r = subprocess.run([cc, *FLAGS, "-O1", *ASAN_HOST, "-c", src, "-o", obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        objs = list(ex.map(compile_one, srcs))
+    r = subprocess.run([cc, f"--offload-arch={ARCH}", *ASAN_HOST, "-o", ASAN_DRIVER, *objs, *kern],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return ASAN_DRIVER
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

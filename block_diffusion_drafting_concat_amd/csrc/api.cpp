@@ -332,6 +332,17 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
   if (!workspace) return fail(DFLASH_ERR_INVALID_ARGUMENT, "workspace is NULL");
   if (cfg->n_layers == 0) return ok();  // nothing to write
 
+  // Every chunk is planned before the first launch: the chunks are full ones of kInjectChunk
+  // rows and one shorter tail, so two plans bound the workspace of the whole call.
+  {
+    size_t need = plan_inject(cfg, std::min(n_rows, kInjectChunk)).total;
+    if (n_rows > kInjectChunk && n_rows % kInjectChunk)
+      need = std::max(need, plan_inject(cfg, n_rows % kInjectChunk).total);
+    if (need > workspace_bytes)
+      return fail(DFLASH_ERR_WORKSPACE_TOO_SMALL, "inject needs %zu workspace bytes, got %zu", need,
+                  workspace_bytes);
+  }
+
   hipStream_t s = (hipStream_t)stream;
   const bool bf = is_bf16(cfg);
   const size_t es = elem_size(cfg);
@@ -339,9 +350,6 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
   for (int r0 = 0; r0 < n_rows; r0 += kInjectChunk) {
     const int rows = std::min(kInjectChunk, n_rows - r0);
     const InjectPlan p = plan_inject(cfg, rows);
-    if (p.total > workspace_bytes)
-      return fail(DFLASH_ERR_WORKSPACE_TOO_SMALL, "inject needs %zu workspace bytes, got %zu", p.total,
-                  workspace_bytes);
     float *y = at<float>(workspace, p.off_y);
     float *ss = at<float>(workspace, p.off_ss);
     float *part = at<float>(workspace, p.off_part);

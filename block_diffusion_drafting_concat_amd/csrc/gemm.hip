@@ -14,8 +14,9 @@
 //    has the CU to itself), so the MFMA loop reads only weights from memory. fp32
 //    activations (one row tile) are moved by LDS DMA: every wave issues global->LDS loads
 //    of 1 KiB segments that need no registers, so a whole pass is in flight at once while
-//    the first weight groups load; the pass is then converted in place to an exact pair of
-//    bf16 values (hi, lo) per element, which costs two MFMAs per step. RMSNorm can be
+//    the first weight groups load; the pass is then converted in place to a pair of bf16
+//    values per element, hi = bf16(f) and lo = bf16(f - hi), which costs two MFMAs per step.
+//    hi + lo keeps 17 significant bits of f (relative error at most 2^-17, about 7.6e-6). RMSNorm can be
 //    applied while converting ("norm on load"): row scales come from per-column-group sums
 //    of squares written by the producer of the rows, the norm weight slice arrives by DMA
 //    with the pass;
@@ -43,10 +44,6 @@ constexpr int kDefaultPassBytes = 60 << 10;  // LDS for one staged A pass unless
 constexpr int kMaxLds = 160 << 10;           // LDS of one CU
 constexpr int kStageVecs = 2;                // A vectors staged per thread per round
 constexpr int kMaxGroupsPerWg = 8;           // column groups of one persistent work-group, max
-#ifndef DFLASH_DMA_STAGING
-#define DFLASH_DMA_STAGING 1
-#endif
-constexpr bool kDmaStaging = DFLASH_DMA_STAGING != 0;  // fp32 activations staged by LDS DMA
 
 // LDS of one staged pass of fp32 activations (DMA staging): rows of whole 1 KiB DMA
 // segments plus 16 bytes of padding (the 16 rows of an MFMA fragment read then fall on
@@ -147,7 +144,7 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
   constexpr bool kF32Src = kAF32 || sizeof(T) == 4;  // A source is fp32
   constexpr int NSRC = kAF32 ? 2 : 1;                // 16-byte source loads per staged vector
   constexpr int TR = 16 * MT, TC = 16 * CW * CT;     // final tile rows, columns
-  constexpr bool kDma = kAF32 && kDmaStaging && MT == 1;
+  constexpr bool kDma = kAF32 && MT == 1;  // fp32 activations of one row tile: LDS DMA staging
   static_assert(!kAF32 || (KPV == 8 && !kMultiA), "fp32 activations pair with bf16 weights");
   // LDS: [A pass][red: NW*NACC*CT*256][fin: NACC*TR*TC]. The A pass is NPL planes of
   // TR x (kp + KPV) elements, or with DMA staging TR rows of dma_row_bytes(kp) then the norm
@@ -636,8 +633,8 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
 // ---- Many rows (M > 64): LDS-tiled MFMA GEMM. A work-group computes a BM x BN tile of
 //      C = A W^T (128 x 128 with 64 x 64 per wave, or 64 x 256 with 32 x 128 per wave; 2 x 2
 //      waves) and walks K in steps of 32. A first pass (split_rows_kernel) normalises the
-//      fp32 activation rows (norm on load) and splits them into the exact (hi, lo) pair of
-//      bf16 planes once, not once per column tile; the weight and activation tiles then go
+//      fp32 activation rows (norm on load) and splits them into a (hi, lo) pair of bf16
+//      planes (17 significant bits of each value) once, not once per column tile; the weight and activation tiles then go
 //      through registers into LDS, the loads of two steps in flight while a step's MFMAs run.
 //      The LDS tiles are [rows][32] bf16 with the 16-byte chunks of a row XOR-swizzled by
 //      (row / 4) % 4, so the 16 rows of a fragment read fall on distinct banks. The tile then
@@ -665,7 +662,8 @@ __device__ __forceinline__ int tile_swz(int row, int c) { return row * 64 + ((c 
 
 // The activations of the tiled GEMM, once per launch: row m of A (the kept rows of the block
 // for the LM head), normalised when the GEMM norms on load (also written to a_out), split into
-// the exact pair of bf16 planes hi [M][K] and lo [M][K] (hi + lo = the fp32 value).
+// two bf16 planes hi [M][K] = bf16(f) and lo [M][K] = bf16(f - hi): hi + lo is the fp32
+// value f to 17 significant bits (relative error at most 2^-17).
 __global__ __launch_bounds__(256) void split_rows_kernel(GemmArgs g, uint16_t *__restrict__ hi,
                                                          uint16_t *__restrict__ lo) {
   __shared__ float red[16];
@@ -997,7 +995,7 @@ hipError_t launch_tiled(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
 template <typename T, int MT, int CW, int CT, int KW, GemmEpi E, bool kAF32>
 size_t lds_bytes(const GemmArgs &g) {
   constexpr int KPV = Storage<T>::kPerVec;
-  const size_t a = kAF32 && kDmaStaging && MT == 1 ? (size_t)16 * dma_row_bytes(g.kp) + dma_w_bytes(g.kp)
+  const size_t a = kAF32 && MT == 1 ? (size_t)16 * dma_row_bytes(g.kp) + dma_w_bytes(g.kp)
                                         : (size_t)16 * MT * (g.kp + KPV) * sizeof(T) * (kAF32 ? 2 : 1);
   const int nacc = E == GemmEpi::kSwiGLU ? 2 : 1;
   const size_t r = ((size_t)CW * KW * nacc * CT * 256 + (size_t)nacc * 16 * MT * 16 * CW * CT) * sizeof(float);
@@ -1236,7 +1234,7 @@ hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, const GemmPla
   auto kp_of = [&](int np) { return ((g.kt + np - 1) / np + step - 1) / step * step; };
   g.kp = kp_of(npass);
   // DMA staging rounds rows up to whole 1 KiB segments: more passes if that overflows
-  while (af32 && kDmaStaging && mt == 1 && g.kp > step && 16 * dma_row_bytes(g.kp) + dma_w_bytes(g.kp) > budget)
+  while (af32 && mt == 1 && g.kp > step && 16 * dma_row_bytes(g.kp) + dma_w_bytes(g.kp) > budget)
     g.kp = kp_of(++npass);
   if (!bf16) return launch_dt<float, false>(g, epi, p, s);
   return af32 ? launch_dt<uint16_t, true>(g, epi, p, s) : launch_dt<uint16_t, false>(g, epi, p, s);

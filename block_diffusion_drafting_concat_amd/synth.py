@@ -49,7 +49,7 @@ class DrafterSpec:
     mask_token_id: int
     rope_theta: float
     rms_eps: float = 1e-6
-    dtype: str = "bf16"  # storage type of weights, activations fed to GEMMs and KV: "bf16"|"f32"
+    dtype: str = "bf16"  # storage type of weights, auxiliary states, the KV cache and the block's q/k/v
 
     @property
     def n_drafts(self) -> int:

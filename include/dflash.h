@@ -18,11 +18,18 @@
  *    follows stream order and is the caller's job. Calls sharing a workspace must not overlap.
  *  - Dense weights are row-major [out_features, in_features] (y = W x). Weights, auxiliary
  *    states and KV caches use the config's storage dtype: bfloat16 (raw 16-bit bf16 values)
- *    or fp32. Activations stay fp32 inside the library (a bf16 GEMM takes them as exact pairs
- *    of bf16 halves); the block's q/k/v are rounded to the storage type like cached K/V. The
- *    RoPE table and hidden_out are fp32. Token ids and positions are int32; slots are int64.
- *  - Host-side validation covers pointers and scalars only; a failing call returns a negative
- *    status, enqueues nothing, and dflash_last_error() (thread-local) explains it. Values in
+ *    or fp32. Activations stay fp32 inside the library; a bf16 GEMM takes each fp32
+ *    activation f as two bf16 values, hi = bf16(f) and lo = bf16(f - hi), whose sum keeps 17
+ *    significant bits of f (relative error at most 2^-17, about 7.6e-6). The block's q/k/v
+ *    are rounded to the storage type like cached K/V. The RoPE table and hidden_out are
+ *    fp32. Token ids and positions are int32; slots are int64.
+ *  - Host-side validation covers pointers and scalars only. A call that fails validation
+ *    (DFLASH_ERR_INVALID_ARGUMENT, DFLASH_ERR_UNSUPPORTED, DFLASH_ERR_WORKSPACE_TOO_SMALL)
+ *    returns before enqueuing anything; every chunk and workspace carve-up of the call is
+ *    planned before its first launch. A DFLASH_ERR_HIP status (a launch the runtime refused)
+ *    can come part-way through a call, after earlier kernels of the same call were enqueued:
+ *    the outputs are then unspecified. dflash_last_error() (thread-local) explains any
+ *    failure. Values in
  *    device memory (positions, sequence lengths, block tables, slots, token ids) are not
  *    validated: out-of-range values are clamped or skipped as each call states, and give
  *    unspecified results but never an out-of-bounds access.
@@ -52,9 +59,15 @@ typedef enum dflash_op { DFLASH_OP_INJECT = 0, DFLASH_OP_PROPOSE = 1 } dflash_op
 
 /* Drafter shape ([N] "Draft Model": a small Qwen3 decoder stack, an fc layer over the
  * concatenated auxiliary states, target embedding and LM head; the DFlashConfig fields
- * block size and mask token id). Supported: head_dim 64 or 128; hidden, intermediate and
- * n_aux*target_hidden multiples of 64; n_q_heads a multiple of n_kv_heads; 2 <= block_size
- * and block_size*n_q_heads/n_kv_heads <= 64 (so block_size - 1 <= 63 drafts). */
+ * block size and mask token id). Every dimension must be positive (n_layers may be 0) and
+ * n_q_heads a multiple of n_kv_heads; mask_token_id in [0, vocab); rms_eps >= 0; dtype
+ * DFLASH_F32 or DFLASH_BF16 (else DFLASH_ERR_INVALID_ARGUMENT). Supported shapes (else
+ * DFLASH_ERR_UNSUPPORTED):
+ *   head_dim 64 or 128;
+ *   hidden, intermediate and n_aux*target_hidden multiples of 128, target_hidden of 32;
+ *   n_q_heads*head_dim a multiple of 128;  hidden <= 16384;  vocab a multiple of 16;
+ *   2 <= block_size <= 64 and block_size*n_q_heads/n_kv_heads <= 64 (so at most 63 drafts);
+ *   n_layers <= 64;  n_aux <= 8. */
 typedef struct dflash_config {
   int32_t hidden;         /* H */
   int32_t n_layers;       /* L */

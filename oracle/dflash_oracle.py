@@ -17,13 +17,19 @@ the docstrings below say "reading" and state the reading taken.
 Storage rounding (reading: the pages fix no precision).  Weights and the KV cache are held in
 the drafter's storage type (bf16 or fp32); the block's own q, k and v, which enter attention
 alongside cached keys and values, are rounded to it as well. Every other activation, including
-every GEMM input, the residual stream, norms, softmax and logits, is kept exact: in fp32 on the
-GPU, where a bf16 GEMM takes an fp32 activation as an exact pair of bf16 halves. Rounding every
-GEMM input instead would make two correct implementations drift apart by about one bf16 unit
-per element after a few layers, since each rounding disagreement is spread by the next dense
-product into the following rounding point. The oracle computes in fp64 and rounds at exactly
-the points above (`rho`). mode="exact" turns all rounding off (a precision diagnostic, and what
-the transformers-based pins compare against).
+every GEMM input, the residual stream, norms, softmax and logits, is kept unrounded here (fp64).
+That too is a reading the pages do not fix: an implementation may keep those activations in
+fp32 and may feed a bf16 matrix unit an approximation of them (for instance the pair
+hi = bf16(f), lo = bf16(f - hi), which keeps 17 significant bits of f); parity tolerances then
+absorb the difference. Rounding every GEMM input to bf16 instead would make two correct
+implementations drift apart by about one bf16 unit per element after a few layers, since each
+rounding disagreement is spread by the next dense product into the following rounding point.
+The oracle computes in fp64 and rounds at exactly the points above (`rho`). mode="exact" turns
+all rounding off (a precision diagnostic, and what the transformers-based pins compare against).
+
+Parity unpinned: the bf16-mode storage rounding points. They are a reading (the pages fix no
+precision), and no pin fixes where rounding happens; the pins below run in mode="exact" or
+check the rounding function itself.
 
 Array conventions: dense weights are row-major [out, in] (y = W x, the F.linear convention).
 Each KV cache is a list over layers of float32 arrays [num_pages, page_size, n_kv_heads,

@@ -87,3 +87,67 @@ def test_workspace_sizes_grow_with_work_and_are_bounded():
     i16 = binding.workspace_bytes(cfg, binding.DFLASH_OP_INJECT, 16)
     ibig = binding.workspace_bytes(cfg, binding.DFLASH_OP_INJECT, 1 << 20)
     assert 0 < i16 < ibig < 1 << 30  # rows are processed in bounded chunks
+
+
+def _dummy_weights(spec):
+    """Weights and cache structs whose every pointer is a non-NULL dummy that must never be
+    dereferenced: a call that passes validation with them would reach the HIP runtime."""
+    vp = ctypes.c_void_p
+    L = spec.n_layers
+    keep = []
+
+    def arr(n, base):
+        a = (vp * max(n, 1))(*[base + 256 * i for i in range(max(n, 1))])
+        keep.append(a)
+        return a
+
+    w = binding.Weights(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000,
+                        *[arr(L, 0x100000 * (i + 1)) for i in range(len(binding._PER_LAYER))],
+                        0x70000, 0x80000, 4096)
+    cache = binding.KvCache(arr(L, 0x9000000), arr(L, 0xA000000), 64, 16, 0xB0000, 4)
+    return w, cache, keep
+
+
+@pytest.mark.parametrize("n_rows", [16, 4096, 4096 + 100, 3 * 4096 + 1])
+def test_inject_checks_every_chunk_before_any_launch(n_rows):
+    """A workspace too small for the call is reported as DFLASH_ERR_WORKSPACE_TOO_SMALL before
+    anything is enqueued: with no GPU here, a call that reached a launch would fail with
+    DFLASH_ERR_HIP instead."""
+    spec = synth.QWEN3_8B_DRAFTER
+    cfg = binding.make_config(spec)
+    w, cache, keep = _dummy_weights(spec)
+    L = binding.lib()
+    aux = (ctypes.c_void_p * spec.n_aux)(*[0xC0000 + 64 * j for j in range(spec.n_aux)])
+    need = binding.workspace_bytes(cfg, binding.DFLASH_OP_INJECT, n_rows)
+    for ws_bytes in (256, need // 2):
+        st = L.dflash_inject_context_kv(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), aux,
+                                        spec.target_hidden, n_rows, 0xD0000, 0xE0000, 0xF0000, ws_bytes, None)
+        assert st == -3, (n_rows, ws_bytes, st, L.dflash_last_error())
+        assert b"workspace" in L.dflash_last_error()
+
+
+def test_propose_checks_workspace_before_any_launch():
+    spec = synth.QWEN3_8B_DRAFTER
+    cfg = binding.make_config(spec)
+    w, cache, keep = _dummy_weights(spec)
+    L = binding.lib()
+    need = binding.workspace_bytes(cfg, binding.DFLASH_OP_PROPOSE, 1, 2048)
+    st = L.dflash_propose_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), 1, 0x1000, 0x2000, 2048,
+                                0x3000, 0x4000, None, 0x5000, need - 1, None)
+    assert st == -3, (st, L.dflash_last_error())
+
+
+def test_header_constraints_match_validation():
+    """Each supported-shape constraint the header lists is the one the library enforces: a
+    config just inside every limit is accepted (workspace sizing succeeds), and stepping over
+    any single limit is rejected."""
+    base = synth.DrafterSpec(hidden=16384, n_layers=64, n_q_heads=4, n_kv_heads=1, head_dim=64,
+                             intermediate=128, vocab=16, n_aux=8, target_hidden=32 * 4, block_size=16,
+                             mask_token_id=15, rope_theta=1e6, dtype="bf16")
+    assert binding.workspace_bytes(binding.make_config(base), binding.DFLASH_OP_INJECT, 1) > 0
+    for bad in [dict(hidden=16384 + 128), dict(n_layers=65), dict(n_aux=9), dict(vocab=24), dict(target_hidden=48),
+                dict(intermediate=192), dict(head_dim=32), dict(block_size=17), dict(block_size=65, n_q_heads=1),
+                dict(n_q_heads=1, n_kv_heads=1)]:
+        spec = replace(base, **bad)
+        cfg = binding.make_config(spec)
+        assert binding.workspace_bytes(cfg, binding.DFLASH_OP_INJECT, 1) == 0, bad
