@@ -70,13 +70,15 @@ def lib() -> ctypes.CDLL:
                                                _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dflash_propose_block.argtypes = [P(Config), P(Weights), P(KvCache), _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                            _vp, ctypes.c_size_t, _vp]
+        L.dflash_propose_block_noalloc.argtypes = [P(Config), P(Weights), P(KvCache), _i32, _vp, _vp, _i32, _vp, _vp,
+                                                   _vp, _vp]
         L.dflash_greedy_verify.argtypes = [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
         L.dflash_greedy_verify_stats.argtypes = [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.dflash_prepare_proposal_inputs.argtypes = [_i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32,
                                                      _vp, _vp, _vp, _vp, _vp]
         for fn in ("dflash_build_rope_table", "dflash_build_fused_kv_weight", "dflash_inject_context_kv",
-                   "dflash_propose_block", "dflash_greedy_verify", "dflash_greedy_verify_stats",
-                   "dflash_prepare_proposal_inputs"):
+                   "dflash_propose_block", "dflash_propose_block_noalloc", "dflash_greedy_verify",
+                   "dflash_greedy_verify_stats", "dflash_prepare_proposal_inputs"):
             getattr(L, fn).restype = _i32
         L.dflash_profile_enable.argtypes = [_i32]
         L.dflash_profile_enable.restype = _i32
@@ -150,6 +152,14 @@ def propose_block(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, dra
                                       _ptr(bonus_tokens), _ptr(seq_lens), max_context, _ptr(draft_token_ids),
                                       _ptr(drafts_only), _ptr(hidden_out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def propose_block_noalloc(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, draft_token_ids, drafts_only,
+                          hidden_out, stream=None) -> None:
+    _check(lib().dflash_propose_block_noalloc(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), batch,
+                                              _ptr(bonus_tokens), _ptr(seq_lens), max_context,
+                                              _ptr(draft_token_ids), _ptr(drafts_only), _ptr(hidden_out),
+                                              _stream(stream)))
 
 
 def greedy_verify(batch, num_drafts, draft_tokens, target_tokens, accepted_len, output_tokens, next_bonus,
@@ -248,6 +258,18 @@ class Drafter:
                    torch.empty((B, K), dtype=torch.int32, device=bonus.device))
         propose_block(self.cfg, self.struct, cache.struct, B, bonus, seq_lens, max_context, out[0], out[1],
                       hidden_out, workspace, stream)
+        return out
+
+    def propose_noalloc(self, cache: PagedCache, bonus, seq_lens, max_context: int, out=None, hidden_out=None,
+                        stream=None):
+        """propose() on the library's static device scratch (no workspace)."""
+        B = int(bonus.shape[0])
+        K = self.spec.block_size - 1
+        if out is None:
+            out = (torch.empty((B, K + 1), dtype=torch.int32, device=bonus.device),
+                   torch.empty((B, K), dtype=torch.int32, device=bonus.device))
+        propose_block_noalloc(self.cfg, self.struct, cache.struct, B, bonus, seq_lens, max_context, out[0], out[1],
+                              hidden_out, stream)
         return out
 
 

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/dflash.h"
@@ -389,14 +390,23 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
   return ok();
 }
 
-dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weights *w, const dflash_kv_cache *cache,
-                                   int32_t batch, const int32_t *bonus_tokens, const int32_t *seq_lens,
-                                   int32_t max_context, int32_t *draft_token_ids, int32_t *drafts_only,
-                                   float *hidden_out, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// Validation of a propose call (everything but the workspace pointer) and its plan. Returns
+// DFLASH_OK with *nothing = true for an empty batch.
+dflash_status propose_check(const dflash_config *cfg, const dflash_weights *w, const dflash_kv_cache *cache,
+                            int32_t batch, const int32_t *bonus_tokens, const int32_t *seq_lens, int32_t max_context,
+                            int32_t *draft_token_ids, int32_t *drafts_only, size_t workspace_bytes,
+                            ProposePlan *plan, bool *nothing) {
+  *nothing = false;
   dflash_status st = check_config(cfg);
   if (st != DFLASH_OK) return st;
   if (batch < 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "batch < 0");
-  if (batch == 0) return ok();
+  if (batch == 0) {
+    *nothing = true;
+    return DFLASH_OK;
+  }
   if (max_context < 0) return fail(DFLASH_ERR_INVALID_ARGUMENT, "max_context < 0");
   if ((st = check_weights_common(cfg, w)) != DFLASH_OK) return st;
   if ((st = check_cache(cfg, cache)) != DFLASH_OK) return st;
@@ -412,14 +422,21 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
     if (!w->in_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->q_norm[l] || !w->wo[l] || !w->post_norm[l] ||
         !w->w_gate[l] || !w->w_up[l] || !w->w_down[l])
       return fail(DFLASH_ERR_INVALID_ARGUMENT, "a weight of layer %d is NULL", l);
-  if (!bonus_tokens || !seq_lens || !draft_token_ids || !drafts_only || !workspace)
+  if (!bonus_tokens || !seq_lens || !draft_token_ids || !drafts_only)
     return fail(DFLASH_ERR_INVALID_ARGUMENT, "an input/output pointer is NULL");
-
-  const ProposePlan p = plan_propose(cfg, batch, max_context);
-  if (p.total > workspace_bytes)
-    return fail(DFLASH_ERR_WORKSPACE_TOO_SMALL, "propose needs %zu workspace bytes, got %zu", p.total,
+  *plan = plan_propose(cfg, batch, max_context);
+  if (plan->total > workspace_bytes)
+    return fail(DFLASH_ERR_WORKSPACE_TOO_SMALL, "propose needs %zu workspace bytes, got %zu", plan->total,
                 workspace_bytes);
+  return DFLASH_OK;
+}
 
+// The launch sequence of a validated propose call on the workspace `workspace`.
+dflash_status propose_enqueue(const dflash_config *cfg, const dflash_weights *w, const dflash_kv_cache *cache,
+                              int32_t batch, const int32_t *bonus_tokens, const int32_t *seq_lens,
+                              int32_t max_context, int32_t *draft_token_ids, int32_t *drafts_only, float *hidden_out,
+                              void *workspace, const ProposePlan &p, void *stream) {
+  const int L = cfg->n_layers;
   hipStream_t s = (hipStream_t)stream;
   const bool bf = is_bf16(cfg);
   const int H = cfg->hidden, D = cfg->head_dim, QH = cfg->n_q_heads, KVH = cfg->n_kv_heads;
@@ -531,6 +548,71 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
   HIP_TRY(launch_argmax_reduce(batch, K, p.lm.col_groups, gl.amax_val, gl.amax_idx, bonus_tokens, cfg->vocab,
                                draft_token_ids, drafts_only, s));
   return ok();
+}
+
+// The static scratch of dflash_propose_block_noalloc: one copy per GPU the library runs on,
+// held until the process ends. In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kStaticScratchBytes = (size_t)DFLASH_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first call on a device).
+dflash_status static_scratch(void **out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DFLASH_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(DFLASH_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DFLASH_OK;
+}
+}  // namespace
+
+extern "C" {
+
+dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weights *w, const dflash_kv_cache *cache,
+                                   int32_t batch, const int32_t *bonus_tokens, const int32_t *seq_lens,
+                                   int32_t max_context, int32_t *draft_token_ids, int32_t *drafts_only,
+                                   float *hidden_out, void *workspace, size_t workspace_bytes, void *stream) {
+  ProposePlan p{};
+  bool nothing = false;
+  dflash_status st = propose_check(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, draft_token_ids,
+                                   drafts_only, workspace_bytes, &p, &nothing);
+  if (st != DFLASH_OK) return st;
+  if (nothing) return ok();
+  if (!workspace) return fail(DFLASH_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  return propose_enqueue(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, draft_token_ids, drafts_only,
+                         hidden_out, workspace, p, stream);
+}
+
+dflash_status dflash_propose_block_noalloc(const dflash_config *cfg, const dflash_weights *w,
+                                           const dflash_kv_cache *cache, int32_t batch, const int32_t *bonus_tokens,
+                                           const int32_t *seq_lens, int32_t max_context, int32_t *draft_token_ids,
+                                           int32_t *drafts_only, float *hidden_out, void *stream) {
+  ProposePlan p{};
+  bool nothing = false;
+  dflash_status st = propose_check(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, draft_token_ids,
+                                   drafts_only, kStaticScratchBytes, &p, &nothing);
+  if (st != DFLASH_OK) {
+    if (st == DFLASH_ERR_WORKSPACE_TOO_SMALL)
+      return fail(st, "propose needs %zu bytes of scratch; the static scratch holds %zu (use dflash_propose_block "
+                  "with a workspace)", p.total, kStaticScratchBytes);
+    return st;
+  }
+  if (nothing) return ok();
+  void *ws = nullptr;
+  if ((st = static_scratch(&ws)) != DFLASH_OK) return st;
+  return propose_enqueue(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, draft_token_ids, drafts_only,
+                         hidden_out, ws, p, stream);
 }
 
 namespace {

@@ -183,6 +183,27 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
                                    int32_t *drafts_only, float *hidden_out, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/* Bytes of the static device scratch that dflash_propose_block_noalloc uses (per GPU). */
+#define DFLASH_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* Block proposal for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The same computation, arguments,
+ * outputs and errors as dflash_propose_block, without the workspace: the call runs on the
+ * library's static device scratch of DFLASH_STATIC_SCRATCH_BYTES, one copy per GPU, held from
+ * the first call on that GPU until the process ends. It allocates nothing and calls no
+ * allocating routine. A call whose workspace would exceed the scratch (dflash_workspace_bytes
+ * of DFLASH_OP_PROPOSE for this batch and max_context) returns DFLASH_ERR_WORKSPACE_TOO_SMALL
+ * before enqueuing anything; 64 MiB holds a Qwen3-8B-shaped batch-1 proposal up to a
+ * 32768-token context. `stream` must belong to the calling thread's current device. Every
+ * call on a GPU shares that GPU's scratch, and the kernels clear what must start at zero, so
+ * calls in stream order need nothing between them; calls that overlap on one GPU (other
+ * streams, other threads) race on the scratch and give unspecified results. */
+dflash_status dflash_propose_block_noalloc(const dflash_config *cfg, const dflash_weights *w,
+                                           const dflash_kv_cache *cache, int32_t batch,
+                                           const int32_t *bonus_tokens, const int32_t *seq_lens,
+                                           int32_t max_context, int32_t *draft_token_ids,
+                                           int32_t *drafts_only, float *hidden_out, void *stream);
+
 /* Greedy verification ([N] "Async Rejection and Position Correction": rejected entries are
  * -1; [Q]: verification by the frozen target gives output identical to standard decoding).
  * target_tokens[b, i] is the target's argmax after the context and draft_tokens[b, :i].

@@ -151,3 +151,21 @@ def test_header_constraints_match_validation():
         spec = replace(base, **bad)
         cfg = binding.make_config(spec)
         assert binding.workspace_bytes(cfg, binding.DFLASH_OP_INJECT, 1) == 0, bad
+
+
+def test_noalloc_propose_rejects_calls_beyond_the_static_scratch():
+    """dflash_propose_block_noalloc checks its plan against the 64 MiB static scratch before
+    it touches the HIP runtime (no GPU here: a call that got further would return -4)."""
+    spec = synth.QWEN3_8B_DRAFTER
+    cfg = binding.make_config(spec)
+    w, cache, keep = _dummy_weights(spec)
+    L = binding.lib()
+    assert binding.workspace_bytes(cfg, binding.DFLASH_OP_PROPOSE, 32, 8192) > 64 << 20
+    st = L.dflash_propose_block_noalloc(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), 32, 0x1000, 0x2000,
+                                        8192, 0x3000, 0x4000, None, None)
+    assert st == -3 and b"static scratch" in L.dflash_last_error()
+    assert L.dflash_propose_block_noalloc(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), 0, None, None, 0,
+                                          None, None, None, None) == 0
+    bad = binding.make_config(replace(spec, head_dim=96))
+    assert L.dflash_propose_block_noalloc(ctypes.byref(bad), None, None, 1, None, None, 0, None, None, None,
+                                          None) == -2
