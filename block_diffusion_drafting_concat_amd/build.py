@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdflash.so")
-SOURCES = ["api.cpp", "profile.cpp", "gemm.hip", "attention.hip", "rowwise.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "gemm.hip", "attention.hip", "rowwise.hip", "persist.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are kept out of every kernel (hipcc would otherwise form them
 # from plain float code).
@@ -69,7 +69,7 @@ def build_asan_driver() -> str:
     of the executable."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
-    kern = [os.path.join(BUILD, n) for n in ("gemm.o", "attention.o", "rowwise.o")]
+    kern = [os.path.join(BUILD, n) for n in ("gemm.o", "attention.o", "rowwise.o", "persist.o")]
     if not all(os.path.exists(k) for k in kern):
         build()
     srcs = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "profile.cpp"),

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 
@@ -129,7 +130,9 @@ InjectPlan plan_inject(const dflash_config *c, int rows) {
 struct ProposePlan {
   int B, M, Mk;
   GemmPlan qkv, o, gu, down, lm;
-  int chunk, nsplit, n_ctr;
+  PlkPlan plk;  // the persistent layer-stack kernel (batch 1), when it applies
+  size_t off_plk;
+  int chunk, nsplit, n_ctr, n_zero;  // n_zero: counters + the persistent kernel's sync words
   size_t off_x, off_ss, off_part, off_ctr, off_q, off_k, off_v, off_o, off_act, off_po, off_pm, off_pl, off_amv,
       off_ami, off_split, total;
 };
@@ -150,6 +153,9 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
   p.down = gemm_plan(M, H, I, D, bf, GemmEpi::kResidAdd, false);
   p.lm = gemm_plan(std::max(p.Mk, 1), c->vocab, H, D, bf, GemmEpi::kArgmax, false);
   attn_plan(B, KVH, max_ctx + c->block_size, &p.chunk, &p.nsplit);
+  p.plk = c->n_layers <= kPlkMaxLayers
+              ? plk_plan(c->n_layers, H, QH, KVH, D, I, c->block_size, B, max_ctx, bf)
+              : PlkPlan{};
   p.n_ctr = std::max(std::max(std::max(gemm_tiles(p.qkv), gemm_tiles(p.o)), std::max(gemm_tiles(p.gu), gemm_tiles(p.down))),
                      gemm_tiles(p.lm));
   const size_t part = std::max(std::max(std::max(gemm_part_floats(p.qkv, M, nqkv, GemmEpi::kHeadNormRope),
@@ -165,7 +171,8 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
   p.off_x = cv.take((size_t)M * H * sizeof(float));
   p.off_ss = cv.take((size_t)ss_groups * M * sizeof(float));
   p.off_part = cv.take(part * sizeof(float));
-  p.off_ctr = cv.take((size_t)p.n_ctr * sizeof(unsigned));
+  p.n_zero = p.n_ctr + (p.plk.ok ? p.plk.sync_words : 0);
+  p.off_ctr = cv.take((size_t)p.n_zero * sizeof(unsigned));
   p.off_q = cv.take((size_t)M * QH * D * es);
   p.off_k = cv.take((size_t)M * KVH * D * es);
   p.off_v = cv.take((size_t)M * KVH * D * es);
@@ -185,7 +192,10 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
   p.off_split = cv.take(2 * split * sizeof(uint16_t));
   p.off_amv = cv.take((size_t)p.lm.col_groups * std::max(p.Mk, 1) * sizeof(float));
   p.off_ami = cv.take((size_t)p.lm.col_groups * std::max(p.Mk, 1) * sizeof(int32_t));
+  p.off_plk = p.plk.ok ? cv.take(p.plk.bytes) : 0;
   p.total = cv.off;
+  // the persistent kernel addresses the workspace with 32-bit offsets
+  if (p.total >= (size_t(1) << 31)) p.plk.ok = 0;
   return p;
 }
 
@@ -452,10 +462,62 @@ dflash_status propose_enqueue(const dflash_config *cfg, const dflash_weights *w,
   float *act = at<float>(workspace, p.off_act);
   uint16_t *asplit = at<uint16_t>(workspace, p.off_split);
 
-  HIP_TRY(launch_embed(bf, w->embed, cfg->vocab, H, bonus_tokens, batch, bs, cfg->mask_token_id, x, ss, ctr, p.n_ctr,
-                       s));
+  HIP_TRY(launch_embed(bf, w->embed, cfg->vocab, H, bonus_tokens, batch, bs, cfg->mask_token_id, x, ss, ctr,
+                       p.n_zero, s));
   int ss_groups = 1;  // column groups of the last producer of x (the embedding: one)
-  for (int l = 0; l < L; ++l) {
+  const unsigned *plk_abort = nullptr;
+  // the persistent layer-stack kernel, when asked for (it addresses one layer's cache with
+  // 32-bit offsets)
+  const char *plk_env = getenv("DFLASH_PERSISTENT_LAYERS");
+  const bool use_plk = plk_env && plk_env[0] == '1' && p.plk.ok &&
+                       (size_t)cache->num_pages * cache->page_size * KVH * D * 2 < (size_t(1) << 31);
+  if (use_plk) {
+    // the whole layer stack in one persistent launch; it leaves the final rows in x and their
+    // sums of squares per 128-column tile in ss
+    PlkArgs pa{};
+    for (int l = 0; l < L; ++l) {
+      PlkLayerW &lw = pa.lw[l];
+      lw.in_norm = static_cast<const uint16_t *>(w->in_norm[l]);
+      lw.wq = static_cast<const uint16_t *>(w->wq[l]);
+      lw.wk = static_cast<const uint16_t *>(w->wk[l]);
+      lw.wv = static_cast<const uint16_t *>(w->wv[l]);
+      lw.q_norm = static_cast<const uint16_t *>(w->q_norm[l]);
+      lw.k_norm = static_cast<const uint16_t *>(w->k_norm[l]);
+      lw.wo = static_cast<const uint16_t *>(w->wo[l]);
+      lw.post_norm = static_cast<const uint16_t *>(w->post_norm[l]);
+      lw.wg = static_cast<const uint16_t *>(w->w_gate[l]);
+      lw.wu = static_cast<const uint16_t *>(w->w_up[l]);
+      lw.wd = static_cast<const uint16_t *>(w->w_down[l]);
+      lw.kc = static_cast<const uint16_t *>(cache->k[l]);
+      lw.vc = static_cast<const uint16_t *>(cache->v[l]);
+    }
+    pa.L = L, pa.H = H, pa.QH = QH, pa.KVH = KVH, pa.I = I, pa.bs = bs, pa.G = QH / KVH;
+    pa.eps = cfg->rms_eps;
+    pa.rope_cos = w->rope_cos, pa.rope_sin = w->rope_sin, pa.rope_max_pos = w->rope_max_pos;
+    pa.seq_lens = seq_lens, pa.max_ctx = max_context;
+    pa.block_table = cache->block_table, pa.maxb = cache->max_blocks_per_seq, pa.P = cache->page_size;
+    pa.num_pages = cache->num_pages;
+    for (int i = 0; i < 4; ++i) pa.g[i] = p.plk.g[i];
+    pa.ntile = p.plk.ntile, pa.ns = p.plk.ns, pa.nwg = p.plk.nwg;
+    pa.rm = p.plk.rm, pa.nrp = p.plk.nrp;
+    char *base = at<char>(workspace, p.off_plk);
+    pa.x0 = x, pa.ss0 = ss;
+    pa.xs = reinterpret_cast<float *>(base + p.plk.off_xs);
+    pa.sss = reinterpret_cast<float *>(base + p.plk.off_sss);
+    pa.qkv = reinterpret_cast<uint16_t *>(base + p.plk.off_qkv);
+    pa.o = reinterpret_cast<float *>(base + p.plk.off_o);
+    pa.act = reinterpret_cast<float *>(base + p.plk.off_act);
+    pa.apo = reinterpret_cast<float *>(base + p.plk.off_apo);
+    pa.apm = reinterpret_cast<float *>(base + p.plk.off_apm);
+    pa.apl = reinterpret_cast<float *>(base + p.plk.off_apl);
+    for (int i = 0; i < 4; ++i) pa.gpart[i] = reinterpret_cast<float *>(base + p.plk.off_gpart[i]);
+    pa.sync = ctr + p.n_ctr;
+    pa.ws = workspace, pa.ws_bytes = (unsigned)p.total;
+    plk_abort = pa.sync + p.plk.sync_words - 1;
+    HIP_TRY(launch_plk(pa, s));
+    ss_groups = H / 128;
+  }
+  for (int l = 0; l < (use_plk ? 0 : L); ++l) {
     // input_layernorm on load; q | k | v in one pass; q/k norm + RoPE in the epilogue
     GemmArgs g = gemm_args(cfg, "gemm.qkv", x, H, M, (QH + 2 * KVH) * D, H, ctr, part);
     g.a_split = asplit;
@@ -546,7 +608,7 @@ dflash_status propose_enqueue(const dflash_config *cfg, const dflash_weights *w,
   gl.amax_idx = at<int32_t>(workspace, p.off_ami);
   HIP_TRY(launch_gemm(gl, bf, GemmEpi::kArgmax, p.lm, s));
   HIP_TRY(launch_argmax_reduce(batch, K, p.lm.col_groups, gl.amax_val, gl.amax_idx, bonus_tokens, cfg->vocab,
-                               draft_token_ids, drafts_only, s));
+                               plk_abort, draft_token_ids, drafts_only, s));
   return ok();
 }
 

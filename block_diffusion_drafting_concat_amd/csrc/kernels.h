@@ -118,10 +118,11 @@ hipError_t launch_embed(bool bf16, const void *embed, int V, int H, const int32_
 hipError_t launch_zero(unsigned *p, int n, hipStream_t s);
 
 // Final argmax over the column groups val/idx [B*K][ngroups] (lowest index on ties) and
-// output assembly.
+// output assembly. With `abort_word` set and nonzero (the persistent layer kernel gave up on a
+// wait), every draft is -1.
 hipError_t launch_argmax_reduce(int B, int K, int ngroups, const float *val, const int32_t *idx,
-                                const int32_t *bonus, int V, int32_t *draft_ids, int32_t *drafts_only,
-                                hipStream_t s);
+                                const int32_t *bonus, int V, const unsigned *abort_word, int32_t *draft_ids,
+                                int32_t *drafts_only, hipStream_t s);
 
 // stats (optional, [3] int64): += B, B*K, sum(acc - 1)
 hipError_t launch_verify(int B, int K, const int32_t *drafts, const int32_t *target, int32_t *acc, int32_t *out,
@@ -154,5 +155,69 @@ struct AttnArgs {
 };
 void attn_plan(int B, int KVH, int max_keys, int *chunk, int *nsplit);
 hipError_t launch_attention(bool bf16, const AttnArgs &a, hipStream_t s);
+
+// ------------------------------------------------------------------------------------------
+// Persistent layer-stack kernel for one block of at most 16 rows (batch 1), bf16 drafters with
+// head_dim 128: every layer's QKV, attention, split merge, O, gate|up and down projections run
+// as jobs of one launch with one work-group per CU. Each work-group has four compute waves
+// (weights -> MFMA, the next chunk's weights always in flight), a stager wave (waits for the
+// producer tiles a job reads, stages its activations in LDS) and a finisher wave (split-K
+// partials, the last contributor's reduction and epilogue, readiness flags). A job waits only
+// for the producer tiles that cover its K range; the RMSNorm row scale of a normalised GEMM
+// input is applied in the reducer's epilogue, so no phase needs a grid-wide barrier.
+// ------------------------------------------------------------------------------------------
+constexpr int kPlkMaxLayers = 8;
+
+struct PlkLayerW {
+  const uint16_t *in_norm, *wq, *wk, *wv, *q_norm, *k_norm, *wo, *post_norm, *wg, *wu, *wd;
+  const uint16_t *kc, *vc;  // this layer's paged cache [num_pages * P][KVH][128]
+};
+
+// One GEMM phase: `tiles` output tiles of 128 columns, `chunks` K chunks of `kr` columns per
+// tile; the tiles x chunks units are dealt to the work-groups in contiguous ranges (base or
+// base + 1 units each, the first `rem` work-groups one more); `slots` bounds the work-groups
+// that share one tile.
+struct PlkGemm {
+  int tiles, chunks, kr, base, rem, slots;
+};
+
+struct PlkArgs {
+  PlkLayerW lw[kPlkMaxLayers];
+  int L, H, QH, KVH, I, bs, G;
+  float eps;
+  const float *rope_cos, *rope_sin;
+  int rope_max_pos;
+  const int32_t *seq_lens;
+  int max_ctx;
+  const int32_t *block_table;
+  int maxb, P, num_pages;
+  PlkGemm g[4];   // QKV, O, gate|up, down
+  int ntile, ns;  // 64-key tiles of the longest key range, splits per kv head
+  int rm, nrp;    // block rows per attention merge job, row groups per q head
+  int nwg;
+  // workspace
+  float *x0, *ss0;         // embedding rows [16][H] and sums of squares [1][16]; also the final
+                           // rows and their sums of squares per 128-column tile [H/128][16]
+  float *xs, *sss;         // x_1 .. x_{2L-1} [2L-1][16][H]; their sums of squares [2L-1][H/128][16]
+  uint16_t *qkv;           // the block's q | k | v per layer [L][16][(QH + 2 KVH) * 128]
+  float *o, *act;          // merged attention output [L][16][QH * 128]; SwiGLU product [L][16][I]
+  float *apo, *apm, *apl;  // attention partials [KVH][ns][64][128], [KVH][ns][64] (reused by layers)
+  float *gpart[4];         // GEMM partials [tiles][slots][nacc][16][128] (reused by layers)
+  unsigned *sync;          // counters, flags and the abort word (zero before the launch)
+  const void *ws;          // the workspace holding every buffer above (ws_bytes < 2^31)
+  unsigned ws_bytes;
+};
+
+struct PlkPlan {
+  int ok;
+  PlkGemm g[4];
+  int ntile, ns, rm, nrp, nwg;
+  size_t off_xs, off_sss, off_qkv, off_o, off_act, off_apo, off_apm, off_apl, off_gpart[4];
+  size_t bytes;   // workspace bytes of the regions above (from offset 0)
+  int sync_words;  // counters + flags + abort word
+};
+// The plan of the persistent kernel for this shape, or ok = 0 when it does not apply.
+PlkPlan plk_plan(int L, int H, int QH, int KVH, int D, int I, int bs, int batch, int max_ctx, bool bf16);
+hipError_t launch_plk(const PlkArgs &a, hipStream_t s);
 
 }  // namespace dflash

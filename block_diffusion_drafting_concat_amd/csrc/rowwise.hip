@@ -53,6 +53,7 @@ __global__ void zero_kernel(unsigned *p, int n) {
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(int B, int K, int ngroups, const float *__restrict__ val,
                                                             const int32_t *__restrict__ idx,
                                                             const int32_t *__restrict__ bonus, int V,
+                                                            const unsigned *__restrict__ abort_word,
                                                             int32_t *__restrict__ draft_ids,
                                                             int32_t *__restrict__ drafts_only) {
   __shared__ float sv[4];
@@ -78,6 +79,7 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(int B, int K, int ng
   if (threadIdx.x != 0) return;
   for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_merge(best, bi, sv[w], si[w]);
   if (bi == 0x7fffffff) bi = 0;  // every logit NaN: unspecified, but a valid id
+  if (abort_word && *abort_word) bi = -1;  // the layer stack did not complete: no draft
   const int b = r / K, j = r % K;
   drafts_only[(size_t)b * K + j] = bi;
   draft_ids[(size_t)b * (K + 1) + j + 1] = bi;
@@ -180,10 +182,11 @@ hipError_t launch_zero(unsigned *p, int n, hipStream_t s) {
 }
 
 hipError_t launch_argmax_reduce(int B, int K, int ngroups, const float *val, const int32_t *idx,
-                                const int32_t *bonus, int V, int32_t *draft_ids, int32_t *drafts_only,
-                                hipStream_t s) {
+                                const int32_t *bonus, int V, const unsigned *abort_word, int32_t *draft_ids,
+                                int32_t *drafts_only, hipStream_t s) {
   ProfScope prof("argmax_reduce", s);
-  argmax_reduce_kernel<<<B * K, 256, 0, s>>>(B, K, ngroups, val, idx, bonus, V, draft_ids, drafts_only);
+  argmax_reduce_kernel<<<B * K, 256, 0, s>>>(B, K, ngroups, val, idx, bonus, V, abort_word, draft_ids,
+                                             drafts_only);
   return hipGetLastError();
 }
 

@@ -175,7 +175,13 @@ dflash_status dflash_inject_context_kv(const dflash_config *cfg, const dflash_we
  *   [batch], clamped to [0, V).  Outputs: draft_token_ids [batch, bs] = [bonus, drafts],
  *   drafts_only [batch, K], and optionally hidden_out [batch*K, H] (fp32): the
  *   final-norm rows fed to the LM head (NULL skips it).
- * batch == 0 returns DFLASH_OK and does nothing. */
+ * batch == 0 returns DFLASH_OK and does nothing.
+ * With DFLASH_PERSISTENT_LAYERS=1 in the environment at the call, a batch-1 bf16 proposal
+ * (head_dim 128, hidden, n_q_heads * 128 and intermediate multiples of 256, at most 8 layers,
+ * block_size <= 16) runs the layer stack as one persistent launch in place of a launch per
+ * projection: the same computation within the same tolerances, off by default (on MI355X it
+ * measured slower than the per-projection launches at the Qwen3-8B shape). Its work-groups
+ * wait for each other with bounded waits; if one gives up (about a second), every draft is -1. */
 dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weights *w,
                                    const dflash_kv_cache *cache, int32_t batch,
                                    const int32_t *bonus_tokens, const int32_t *seq_lens,
