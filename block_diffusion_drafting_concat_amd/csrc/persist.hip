@@ -47,13 +47,14 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "stream_core.h"
 
 namespace dflash {
 namespace {
+using namespace wave;
 
 constexpr int kStagers = 3;  // stager waves 4..6: job k is staged by wave 4 + k % 3
 constexpr int kWaves = 4 + kStagers + 1, kThreads = kWaves * 64;
-constexpr int kTN = 128;    // output columns of a tile
 constexpr int kD = 128;     // head dim
 constexpr int kKrMax = 256;  // K columns of a chunk (one weight matrix)
 constexpr int kArow = kKrMax * 4 + 16;  // LDS bytes of one staged row: 32 B per 8 columns + pad
@@ -64,81 +65,9 @@ constexpr int kAttnBytes = (64 * kQs + 64 * kKs + kD * kVs) * 2;  // an attentio
 constexpr int kOslot = 16 * kTN * 4 * 2;  // one output slot (16 KiB)
 constexpr int kLds = kNA * kAslot + 2 * kOslot;  // plus the job list
 static_assert(kAttnBytes <= kNA * kAslot, "an attention tile fits the activation slots");
-constexpr unsigned long long kWaitTicks = 100000000ull;  // 1 s of the 100 MHz real-time clock
 
 enum Stage { kSQkv = 0, kSAttn = 1, kSMerge = 2, kSO = 3, kSGu = 4, kSDown = 5 };
 __device__ __forceinline__ int ph_of(int st) { return st == kSQkv ? 0 : st == kSO ? 1 : st == kSGu ? 2 : 3; }
-
-// ---- agent-coherent accesses (relaxed atomics at agent scope)
-__device__ __forceinline__ uint64_t ldc64(const void *p) {
-  return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void stc64(void *p, uint64_t v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint4 ldc128(const void *p) {
-  const uint64_t a = ldc64(p), b = ldc64(static_cast<const char *>(p) + 8);
-  return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
-}
-__device__ __forceinline__ void stc128(void *p, uint4 v) {
-  stc64(p, v.x | ((uint64_t)v.y << 32));
-  stc64(static_cast<char *>(p) + 8, v.z | ((uint64_t)v.w << 32));
-}
-__device__ __forceinline__ float ldcf(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void stcf(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned ldcu(const unsigned *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void stcu(unsigned *p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Workspace data handed between work-groups goes through a buffer resource over the workspace:
-// 128-bit loads and stores with the same cache policy (sc1) as the agent-scope accesses above, a
-// 32-bit offset per access instead of a 64-bit address.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-constexpr int kSC1 = 16;  // buffer cache-policy bits: sc1
-struct Ws {
-  __amdgpu_buffer_rsrc_t r;
-  const char *base;
-  __device__ int off(const void *p) const { return (int)(static_cast<const char *>(p) - base); }
-};
-__device__ __forceinline__ uint4 wld128(const Ws &ws, const void *p) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(ws.r, ws.off(p), 0, kSC1);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-// the same with the offset split into a per-lane part (VGPR) and a wave-uniform part (SGPR)
-__device__ __forceinline__ uint4 wld128s(const Ws &ws, int voff, int soff) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(ws.r, voff, __builtin_amdgcn_readfirstlane(soff), kSC1);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint64_t wld64(const Ws &ws, const void *p) {
-  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(ws.r, ws.off(p), 0, kSC1);
-  return (uint64_t)v.x | ((uint64_t)v.y << 32);
-}
-__device__ __forceinline__ float wldf(const Ws &ws, const float *p) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ws.r, ws.off(p), 0, kSC1));
-}
-__device__ __forceinline__ void wst128(const Ws &ws, void *p, uint4 v) {
-  const u32x4_t t = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(t, ws.r, ws.off(p), 0, kSC1);
-}
-__device__ __forceinline__ void wst64(const Ws &ws, void *p, uint64_t v) {
-  const u32x2_t t = {(unsigned)v, (unsigned)(v >> 32)};
-  __builtin_amdgcn_raw_buffer_store_b64(t, ws.r, ws.off(p), 0, kSC1);
-}
-__device__ __forceinline__ void wstf(const Ws &ws, float *p, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ws.r, ws.off(p), 0, kSC1);
-}
-
-__device__ __forceinline__ float f2(uint64_t v, int i) { return __uint_as_float((uint32_t)(v >> (32 * i))); }
-__device__ __forceinline__ uint64_t pack2(float a, float b) {
-  return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-}
 
 // ---- sync words: per layer [counters of the 4 GEMM phases][their flags][attention counters per
 //      kv head][merge flags per q head and row group]; the abort word after the last layer
@@ -166,7 +95,6 @@ struct Sync {
 // that waits past the time limit raises both; a wave that sees either stops waiting.
 // (The work-group word is accessed through an LDS pointer: a generic access would also count
 // on the vector-memory counter and wait for every weight load in flight.)
-typedef __attribute__((address_space(3))) volatile int lds_vint;
 struct Abort {
   unsigned *grid;
   int *wg;
@@ -201,9 +129,6 @@ __device__ __forceinline__ void wave_wait(const unsigned *w, int stride, int n, 
 }
 
 // A wave waits until the LDS word *p >= want (hand-offs between the waves of the work-group).
-__device__ __forceinline__ int lds_load(const int *p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
 __device__ __forceinline__ void lds_wait(const int *p, int want, const Abort &ab) {
   if (lds_load(p) >= want) return;
   const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
@@ -215,13 +140,6 @@ __device__ __forceinline__ void lds_wait(const int *p, int want, const Abort &ab
     }
     __builtin_amdgcn_s_sleep(1);
   }
-}
-// One increment per wave (lane 0), ordered after the wave's earlier LDS accesses.
-__device__ __forceinline__ void lds_add(int *p, int v) {
-  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ void lds_set(int *p, int v) {
-  if ((threadIdx.x & 63) == 0) __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // ---- the job list of work-group w: per layer, its QKV units, attention tiles, merge, O, gate|up
@@ -386,60 +304,8 @@ __device__ __forceinline__ GemmSrc gemm_src(const PlkArgs &a, int l, int ph, int
 // =============================================================================================
 // Compute waves
 // =============================================================================================
-struct WBuf {
-  Vec16 v[16];  // [column tile ct][K step]
-};
-
-// 16 bytes of global memory. The weight pointers come from the job list in LDS, which hides
-// their address space from the compiler; a generic (flat) load would also count on the LDS
-// counter, so every LDS wait would wait for the weight loads in flight as well. A pointer made
-// from the integer address is a global one (a cast of the generic pointer stays generic).
-typedef __attribute__((address_space(1))) const u32x4_t global_u32x4_t;
-__device__ __forceinline__ Vec16 load_global16(const void *p) {
-  const u32x4_t t = *(global_u32x4_t *)(uintptr_t)p;
-  Vec16 v;
-  __builtin_memcpy(&v.u, &t, 16);
-  return v;
-}
-
-// Every GEMM job is eight K steps of 32 columns: one matrix with a 256-column chunk, or gate and
-// up with a 128-column chunk each (steps 0-3 gate, 4-7 up). Steps 0-3 accumulate into acc[0],
-// steps 4-7 into acc[1], whatever the job: no branch picks registers, and for one matrix the two
-// halves are added at the flush.
-//
-// Weight loads of GEMM job d for compute wave cw into b (16 loads of 16 B per lane)
 __device__ __forceinline__ void issue_w(const JobD &d, WBuf &b, int cw, int lane) {
-  const int k0 = d.kc * d.kr;
-  const bool dual = d.ph == 2;
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const size_t row = (size_t)(cw * 32 + ct * 16 + (lane & 15)) * d.K + k0 + (lane >> 4) * 8;
-#pragma unroll
-    for (int sp = 0; sp < 8; ++sp) {
-      const bool up = dual && sp >= 4;
-      const int step = dual ? (sp & 3) : sp;
-      b.v[ct * 8 + sp] = load_global16((up ? d.w1 : d.w0) + row + step * 32);
-    }
-  }
-}
-
-// MFMAs of GEMM job d: activations from the LDS slot `sa`, weights from b
-__device__ __forceinline__ void mma_job(const JobD &d, const WBuf &b, const unsigned char *sa, f32x4_t (&acc)[2][2],
-                                        int lane) {
-  const bool dual = d.ph == 2;
-#pragma unroll
-  for (int sp = 0; sp < 8; ++sp) {
-    const int step = dual ? (sp & 3) : sp;
-    const unsigned char *pa = sa + (lane & 15) * kArow + (step * 4 + (lane >> 4)) * 32;
-    Vec16 hi, lo;
-    hi.u = *reinterpret_cast<const uint4 *>(pa);
-    lo.u = *reinterpret_cast<const uint4 *>(pa + 16);
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      mma16<uint16_t>(acc[sp >> 2][ct], hi, b.v[ct * 8 + sp]);
-      mma16<uint16_t>(acc[sp >> 2][ct], lo, b.v[ct * 8 + sp]);
-    }
-  }
+  issue_w(d.w0, d.w1, d.K, d.kc, d.kr, d.ph == 2, b, cw, lane);
 }
 
 // Attention tile of job j for query rows 16 * cw + lane % 16 (the finisher wave runs the four
@@ -601,26 +467,27 @@ __device__ __forceinline__ void stage_gemm(const PlkArgs &a, const Ws &ws, const
   const float rs = (lane & 15) < a.bs ? rsqrtf(ssum / (float)a.H + a.eps) : 0.f;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    if (u >= ng / 4) break;
-    const int row = u * rstep + lane / ng;
-    float f[8];
-    __builtin_memcpy(f, v[u], 32);
-    if (row >= a.bs) {
+    if (u < ng / 4) {
+      const int row = u * rstep + lane / ng;
+      float f[8];
+      __builtin_memcpy(f, v[u], 32);
+      if (row >= a.bs) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = 0.f;
-    }
-    if (s.norm_w) {
-      const float rs_row = __shfl(rs, row, 64);
+        for (int e = 0; e < 8; ++e) f[e] = 0.f;
+      }
+      if (s.norm_w) {
+        const float rs_row = __shfl(rs, row, 64);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] *= bf16_to_f32(w[e]) * rs_row;
-    }
-    uint16_t hl[16];
+        for (int e = 0; e < 8; ++e) f[e] *= bf16_to_f32(w[e]) * rs_row;
+      }
+      uint16_t hl[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      hl[e] = f32_to_bf16(f[e]);
-      hl[8 + e] = f32_to_bf16(f[e] - bf16_to_f32(hl[e]));
+      for (int e = 0; e < 8; ++e) {
+        hl[e] = f32_to_bf16(f[e]);
+        hl[8 + e] = f32_to_bf16(f[e] - bf16_to_f32(hl[e]));
+      }
+      __builtin_memcpy(slot + row * kArow + c8 * 32, hl, 32);
     }
-    __builtin_memcpy(slot + row * kArow + c8 * 32, hl, 32);
   }
 }
 
@@ -788,37 +655,6 @@ __device__ __forceinline__ void merge_stage(const PlkArgs &a, const Ws &ws, cons
 // =============================================================================================
 // Finisher wave
 // =============================================================================================
-// Sum of the count partial tiles at part, in contributor order, into out (LDS): NB contributors
-// per round trip; lane + 64 e is the lane's e-th float4 of the tile.
-template <int NACC>
-__device__ __forceinline__ void reduce_partials(const Ws &ws, const float *part, int count, float *out, int lane) {
-  constexpr int E = 8 * NACC, NB = 24 / E > 0 ? 24 / E : 1;
-  const int voff = ws.off(part) + lane * 16;  // bytes
-  for (int q0 = 0; q0 < count; q0 += NB) {
-    uint4 v[NB][E];
-#pragma unroll
-    for (int qq = 0; qq < NB; ++qq)
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        v[qq][e] = wld128s(ws, voff, (min(q0 + qq, count - 1) * NACC * 16 * kTN + e * 64 * 4) * 4);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float4 *o = reinterpret_cast<float4 *>(out + (e * 64 + lane) * 4);
-      float4 sum = q0 == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : *o;
-#pragma unroll
-      for (int qq = 0; qq < NB; ++qq) {
-        if (q0 + qq < count) {
-          sum.x += __uint_as_float(v[qq][e].x);
-          sum.y += __uint_as_float(v[qq][e].y);
-          sum.z += __uint_as_float(v[qq][e].z);
-          sum.w += __uint_as_float(v[qq][e].w);
-        }
-      }
-      *o = sum;
-    }
-  }
-}
-
 // A flushed tile out[nacc][16][128] (the work-group's partial): with other contributors, store
 // it and count it; the last contributor sums every partial and runs the epilogue (q/k RMSNorm +
 // RoPE; residual add with the rows' per-tile sums of squares; SwiGLU), then raises the flag.
@@ -1052,7 +888,7 @@ __global__ __launch_bounds__(kThreads, 1) void plk_kernel(PlkArgs args) {
     auto gemm_job = [&](WBuf &buf) {
       const JobD d = jobs[k];
       lds_wait(&s_ready[d.gb % kNA], d.gb + 1, ab);
-      mma_job(d, buf, aslot(d.gb), acc, lane);
+      mma_job(d.ph == 2, kArow, buf, aslot(d.gb), acc, lane);
       lds_add(&s_released, 1);
       // (job indices made wave-uniform, so the loop's branches are scalar ones)
       const int k1 = __builtin_amdgcn_readfirstlane(d.ng);
