@@ -634,7 +634,8 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
 //      C = A W^T (128 x 128 with 64 x 64 per wave, or 64 x 256 with 32 x 128 per wave; 2 x 2
 //      waves) and walks K in steps of 32. A first pass (split_rows_kernel) normalises the
 //      fp32 activation rows (norm on load) and splits them into a (hi, lo) pair of bf16
-//      planes (17 significant bits of each value) once, not once per column tile; the weight and activation tiles then go
+//      planes (17 significant bits of each value) once, not once per column tile (the LM
+//      head takes the hi plane alone, see gemm_plan); the weight and activation tiles then go
 //      through registers into LDS, the loads of two steps in flight while a step's MFMAs run.
 //      The LDS tiles are [rows][32] bf16 with the 16-byte chunks of a row XOR-swizzled by
 //      (row / 4) % 4, so the 16 rows of a fragment read fall on distinct banks. The tile then
@@ -981,6 +982,17 @@ hipError_t launch_tiled_shape(const GemmArgs &g, const GemmPlan &p, hipStream_t 
     t.a[0] = hi;
     t.a[1] = lo;
     t.a_nseg = 1;
+    if (p.hi_only) {
+      // the bf16 plane alone, as a single-segment bf16 A
+      t.lda = g.K;
+      auto kern1 = gemm_tiled_kernel<E, false, BM, BN>;
+      static const hipError_t attr1 = hipFuncSetAttribute(
+          reinterpret_cast<const void *>(kern1), hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds - 1024);
+      if (attr1 != hipSuccess) return attr1;
+      kern1<<<(ntiles + 7) / 8 * 8 * mtiles * p.splits, 256, TileLds<BM, BN>::bytes(), s>>>(t, mtiles, ntiles,
+                                                                                            p.splits);
+      return hipGetLastError();
+    }
   }
   kern<<<(ntiles + 7) / 8 * 8 * mtiles * p.splits, 256, TileLds<BM, BN>::bytes(), s>>>(t, mtiles, ntiles,
                                                                                          p.splits);
@@ -1131,6 +1143,11 @@ GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bo
     // one work-group per CU: a second one on a CU shares its LDS and matrix cores and adds
     // little) per unit of work, plus a small cost per extra split for the reduction through
     // the workspace; at least 32 K steps per split.
+    // The LM head's fp32 input rows enter the matrix cores as one bf16 plane (not a hi + lo
+    // pair): half the MFMAs and half the A tile. A CPU study on the batch-128 workload (every
+    // GEMM input rounded to bf16 in turn) changed no draft whose top-2 logit gap is >= 1e-2 when
+    // the LM head's input was rounded.
+    p.hi_only = a_f32 && epi == GemmEpi::kArgmax;
     const long wgs = (long)p.col_groups * p.row_blocks, slots = cu_count();
     p.splits = smin;
     if (smin == 1 && wgs < slots) {

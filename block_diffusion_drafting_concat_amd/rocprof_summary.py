@@ -98,9 +98,30 @@ def pmc(workload: str, fetch_csv: str, write_csv: str) -> dict:
             "scale_fetch": scale_f, "scale_write": scale_w, "kernels": kernels}
 
 
+def counters(paths) -> str:
+    """Per kernel (short name) and counter: dispatches and the mean value per dispatch, over
+    every counter-collection CSV given (one rocprofv3 --pmc run each)."""
+    per = defaultdict(lambda: defaultdict(list))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            per[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for k in per.values() for c in k})
+    out = ["| kernel | " + " | ".join(f"{c} (dispatches, mean)" for c in names) + " |",
+           "|---|" + "---:|" * len(names)]
+    for k in sorted(per, key=lambda k: -max(sum(v) for v in per[k].values())):
+        cells = []
+        for c in names:
+            v = per[k].get(c, [])
+            cells.append(f"{len(v)}, {sum(v) / len(v):.4g}" if v else "")
+        out.append(f"| {k} | " + " | ".join(cells) + " |")
+    return "\n".join(out)
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "stats":
         print(stats(argv[1]))
+    elif len(argv) >= 2 and argv[0] == "counters":
+        print(counters(argv[1:]))
     elif len(argv) >= 4 and argv[0] == "pmc":
         print(json.dumps(pmc(argv[1], argv[2], argv[3]), indent=1))
     else:
