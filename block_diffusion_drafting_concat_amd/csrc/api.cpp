@@ -133,6 +133,7 @@ struct ProposePlan {
   PlkPlan plk;  // the persistent layer-stack kernel (batch 1), when it applies
   size_t off_plk;
   int chunk, nsplit, n_ctr, n_zero;  // n_zero: counters + the persistent kernel's sync words
+  size_t off_items;  // the attention work-group list (several sequences)
   size_t off_x, off_ss, off_part, off_ctr, off_q, off_k, off_v, off_o, off_act, off_po, off_pm, off_pl, off_amv,
       off_ami, off_split, total;
 };
@@ -182,6 +183,7 @@ ProposePlan plan_propose(const dflash_config *c, int B, int max_ctx) {
   p.off_po = cv.take(nrow * D * sizeof(float));
   p.off_pm = cv.take(nrow * sizeof(float));
   p.off_pl = cv.take(nrow * sizeof(float));
+  p.off_items = B > 1 ? cv.take(((size_t)B * KVH * p.nsplit + 1) * sizeof(int)) : 0;
   // the (hi, lo) bf16 planes of the activations of the tiled GEMMs (many rows), reused by each
   size_t split = 0;
   if (p.qkv.tiled) split = std::max(split, (size_t)M * H);
@@ -562,6 +564,12 @@ dflash_status propose_enqueue(const dflash_config *cfg, const dflash_weights *w,
     at_.pm = at<float>(workspace, p.off_pm);
     at_.pl = at<float>(workspace, p.off_pl);
     at_.o = o;
+    if (batch > 1) {
+      // the work-groups that have keys, listed once for every layer (same sequence lengths)
+      int *items = at<int>(workspace, p.off_items), *n_items = items + (size_t)batch * KVH * p.nsplit;
+      if (l == 0) HIP_TRY(launch_attention_items(at_, items, n_items, s));
+      at_.items = items, at_.n_items = n_items;
+    }
     HIP_TRY(launch_attention(bf, at_, s));
 
     // O projection + residual add; the row sums of squares feed the post-attention norm

@@ -28,7 +28,7 @@ namespace {
 constexpr int kTileKeys = 64;
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 3) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
   constexpr int KPV = Storage<T>::kPerVec;
   constexpr int CH = 4 * KPV;                // contraction elements per MFMA step
   constexpr int NB = KPV / 4;                // score tiles per P.V step
@@ -39,7 +39,12 @@ __global__ __launch_bounds__(256, 3) void attn_partial_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T vts[D * VSTR];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  if (a.items) {  // the blockIdx.x-th work-group that has keys (a 1-D grid)
+    if ((int)blockIdx.x >= *a.n_items) return;
+    const int f = a.items[blockIdx.x];
+    split = f % a.nsplit, g = (f / a.nsplit) % a.KVH, b = f / (a.nsplit * a.KVH);
+  }
   const int G = a.QH / a.KVH;
   const int R = a.bs * G;
   const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
@@ -86,7 +91,10 @@ __global__ __launch_bounds__(256, 3) void attn_partial_kernel(AttnArgs a) {
   auto v_kappa = [](int v) { return (v & 15) | (((v >> 6) & 1) << 4); };
   auto v_part = [](int v) { return ((v >> 4) & 3) | ((v >> 7) << 2); };
   int kpg[KVEC], vpg[VVEC][2];
-  Vec16 kreg[KVEC], vreg[VVEC][2];
+  struct TileRegs {
+    Vec16 k[KVEC], v[VVEC][2];
+  };
+  TileRegs ra, rb;  // two tiles' loads in flight: tile n in ra (n even) or rb (n odd)
   auto load_pages = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < KVEC; ++i) {
@@ -107,44 +115,55 @@ __global__ __launch_bounds__(256, 3) void attn_partial_kernel(AttnArgs a) {
     if (ctx) return ((size_t)(min(max(page, 0), a.num_pages - 1) * a.P + t % a.P) * a.KVH + g) * D + part * KPV;
     return ((size_t)(b * a.bs + (t - c)) * a.KVH + g) * D + part * KPV;
   };
-  auto issue = [&](int t0) {
+  // Keys past kend read key kend - 1 (in range; the scores mask them and their V rows are
+  // finite, so they add nothing): every load is unconditional, with no select on its value
+  // before the LDS write, so none waits for another.
+  auto issue = [&](TileRegs &rr, int t0) {
 #pragma unroll
     for (int i = 0; i < KVEC; ++i) {
-      const int v = threadIdx.x + i * 256, t = t0 + v / CPR;
+      const int v = threadIdx.x + i * 256, t = min(t0 + v / CPR, kend - 1);
       bool ctx;
       const size_t off = key_off(t, kpg[i], v % CPR, ctx);
-      kreg[i] = t < kend ? load_vec16((ctx ? kc : kbk) + off) : zero_vec16();
+      rr.k[i] = load_vec16((ctx ? kc : kbk) + off);
     }
 #pragma unroll
     for (int i = 0; i < VVEC; ++i) {
       const int v = threadIdx.x + i * 256;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int t = t0 + 2 * v_kappa(v) + h;
+        const int t = min(t0 + 2 * v_kappa(v) + h, kend - 1);
         bool ctx;
         const size_t off = key_off(t, vpg[i][h], v_part(v), ctx);
-        vreg[i][h] = t < kend ? load_vec16((ctx ? vc : vbk) + off) : zero_vec16();
+        rr.v[i][h] = load_vec16((ctx ? vc : vbk) + off);
       }
     }
   };
+  // Tile n's loads go out two tiles ahead (while tiles n - 2 and n - 1 compute); the page
+  // reads a tile ahead of those.
+  const int ntiles = (kend - kbeg + kTileKeys - 1) / kTileKeys;
   load_pages(kbeg);
-  issue(kbeg);
-  if (kbeg + kTileKeys < kend) load_pages(kbeg + kTileKeys);
+  issue(ra, kbeg);
+  if (ntiles > 1) {
+    load_pages(kbeg + kTileKeys);
+    issue(rb, kbeg + kTileKeys);
+  }
+  if (ntiles > 2) load_pages(kbeg + 2 * kTileKeys);
 
-  for (int t0 = kbeg; t0 < kend; t0 += kTileKeys) {
+  auto tile = [&](TileRegs &rr, int n) {
+    const int t0 = kbeg + n * kTileKeys;
     // ---- the tile's registers into LDS: K row-major, V transposed
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < KVEC; ++i) {
       const int v = threadIdx.x + i * 256;
-      *reinterpret_cast<uint4 *>(&ks[(v / CPR) * KSTR + (v % CPR) * KPV]) = kreg[i].u;
+      *reinterpret_cast<uint4 *>(&ks[(v / CPR) * KSTR + (v % CPR) * KPV]) = rr.k[i].u;
     }
 #pragma unroll
     for (int i = 0; i < VVEC; ++i) {
       const int v = threadIdx.x + i * 256, kap = v_kappa(v), part = v_part(v);
       T v0[KPV], v1[KPV];
-      __builtin_memcpy(v0, &vreg[i][0].u, 16);
-      __builtin_memcpy(v1, &vreg[i][1].u, 16);
+      __builtin_memcpy(v0, &rr.v[i][0].u, 16);
+      __builtin_memcpy(v1, &rr.v[i][1].u, 16);
 #pragma unroll
       for (int e = 0; e < KPV; ++e) {
         T *dst = &vts[(part * KPV + e) * VSTR + 2 * kap];
@@ -156,12 +175,12 @@ __global__ __launch_bounds__(256, 3) void attn_partial_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    // ---- the next tile's loads fly during this tile's compute
-    if (t0 + kTileKeys < kend) {
-      issue(t0 + kTileKeys);
-      if (t0 + 2 * kTileKeys < kend) load_pages(t0 + 2 * kTileKeys);
+    // ---- tile n + 2's loads into the registers just written out
+    if (n + 2 < ntiles) {
+      issue(rr, t0 + 2 * kTileKeys);
+      if (n + 3 < ntiles) load_pages(t0 + 3 * kTileKeys);
     }
-    if (wave * 16 >= R) continue;
+    if (wave * 16 >= R) return;
 
     // ---- S^T tiles: 4 tiles of 16 keys; tile sb row rho holds key
     //      (sb / NB) * CH + KPV * (rho / 4) + 4 * (sb % NB) + rho % 4
@@ -238,7 +257,13 @@ __global__ __launch_bounds__(256, 3) void attn_partial_kernel(AttnArgs a) {
         }
       }
     }
+  };
+  // a counted loop over pairs of tiles, the odd tile after it (each register set keeps its role)
+  for (int n = 0; n + 1 < ntiles; n += 2) {
+    tile(ra, n);
+    tile(rb, n + 1);
   }
+  if (ntiles & 1) tile(ra, ntiles - 1);
   // ---- O^T lane layout: d = db*16 + (lane/16)*4 + i, row r = wave*16 + lane%16
   const bool active = wave * 16 < R;
   if (active) {
@@ -362,9 +387,43 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(AttnArgs a) {
   }
 }
 
+// The work-groups of the partial kernel that have keys, in (sequence, split, kv head) order:
+// one work-group; the sequences' split counts are scanned 256 at a time.
+__global__ __launch_bounds__(256) void attn_items_kernel(AttnArgs a, int *items, int *n_items) {
+  __shared__ int scan[256];
+  __shared__ int carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < a.B; b0 += 256) {
+    const int b = b0 + (int)threadIdx.x;
+    int ns = 0;
+    if (b < a.B) {
+      const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
+      ns = min((c + a.bs + a.chunk - 1) / a.chunk, a.nsplit);
+    }
+    scan[threadIdx.x] = ns;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {  // inclusive scan
+      const int v = threadIdx.x >= (unsigned)o ? scan[threadIdx.x - o] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    const int pre = carry + scan[threadIdx.x] - ns;  // splits of the sequences before b
+    // (sequence, split, kv head) order: the kv heads of one key range are launched together,
+    // and each reads its 256-byte slice of the same 2 KiB cache rows
+    for (int sp = 0; sp < ns; ++sp)
+      for (int gg = 0; gg < a.KVH; ++gg) items[a.KVH * (pre + sp) + gg] = (b * a.KVH + gg) * a.nsplit + sp;
+    __syncthreads();
+    if (threadIdx.x == 255) carry += scan[255];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *n_items = a.KVH * carry;
+}
+
 template <typename T>
 hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
-  dim3 grid(a.nsplit, a.KVH, a.B);
+  dim3 grid = a.items ? dim3(a.nsplit * a.KVH * a.B) : dim3(a.nsplit, a.KVH, a.B);
   {
     ProfScope prof("attn_partial", s);
     if (a.D == 128)
@@ -388,7 +447,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 }  // namespace
 
 void attn_plan(int B, int KVH, int max_keys, int *chunk, int *nsplit) {
-  // Aim for ~768 work-groups in total (one round at three per CU), in splits of at least one
+  // Aim for ~768 work-groups in total (a round and a half at two per CU), in splits of at least one
   // 64-key tile and at most eight: with many sequences of unequal length, short splits keep
   // the work-groups even.
   long want = (long)max_keys * B * KVH / 768;
@@ -401,6 +460,12 @@ void attn_plan(int B, int KVH, int max_keys, int *chunk, int *nsplit) {
 
 hipError_t launch_attention(bool bf16, const AttnArgs &a, hipStream_t s) {
   return bf16 ? launch_t<uint16_t>(a, s) : launch_t<float>(a, s);
+}
+
+hipError_t launch_attention_items(const AttnArgs &a, int *items, int *n_items, hipStream_t s) {
+  ProfScope prof("attn_items", s);
+  attn_items_kernel<<<1, 256, 0, s>>>(a, items, n_items);
+  return hipGetLastError();
 }
 
 }  // namespace dflash

@@ -153,9 +153,15 @@ struct AttnArgs {
   int chunk, nsplit;    // keys per split (multiple of 64), splits per sequence
   float *po, *pm, *pl;  // partials [B][KVH][nsplit][64][D], [B][KVH][nsplit][64]
   float *o;             // merged output [M][QH*D], fp32
+  // With several sequences: the (sequence, kv head, split) work-groups that have keys, as
+  // flat indices (b * KVH + g) * nsplit + split, and their count (written by
+  // launch_attention_items once per proposal); null: every index of the grid is launched.
+  const int *items, *n_items;
 };
 void attn_plan(int B, int KVH, int max_keys, int *chunk, int *nsplit);
 hipError_t launch_attention(bool bf16, const AttnArgs &a, hipStream_t s);
+// items [B * KVH * nsplit] and n_items [1] of `a` from the sequence lengths.
+hipError_t launch_attention_items(const AttnArgs &a, int *items, int *n_items, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------
 // Persistent layer-stack kernel for one block of at most 16 rows (batch 1), bf16 drafters with
