@@ -26,6 +26,7 @@ namespace dflash {
 namespace {
 
 constexpr int kTileKeys = 64;
+constexpr int kMaxChunk = 16 * kTileKeys;  // keys per split at most (attn_plan)
 
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
@@ -37,6 +38,7 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
   constexpr int CPR = D / KPV;               // 16-byte vectors per key row
   __shared__ __attribute__((aligned(16))) T ks[kTileKeys * KSTR];
   __shared__ __attribute__((aligned(16))) T vts[D * VSTR];
+  __shared__ int pgs[kMaxChunk + 1];  // page-table entries of the split's key range
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -47,16 +49,17 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
   }
   const int G = a.QH / a.KVH;
   const int R = a.bs * G;
-  const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
-  const int T_total = c + a.bs;
   const int kbeg = split * a.chunk;
-  if (kbeg >= T_total) return;  // nothing for this split
-  const int kend = min(T_total, kbeg + a.chunk);
-
-  // Query fragment (B operand of S^T): row r = hh*bs + j of this wave's 16-row tile.
-  const int r = wave * 16 + (lane & 15);
+  const int32_t *bt = a.block_table + (size_t)b * a.maxb;
+  // The context length, the query fragment and the page-table entries of the split's key
+  // range are loaded together (one round trip): the page entries cover keys [kbeg, kbeg +
+  // chunk) whatever the length, clamped into the table, and go to LDS, so that the K/V loads
+  // of later tiles read them there instead of waiting behind the loads in flight.
+  const int pbeg = kbeg / a.P, npg = (a.chunk - 1) / a.P + 2;
+  const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
+  const int r = wave * 16 + (lane & 15);  // query row hh*bs + j of this wave's 16-row tile
   const bool rvalid = r < R && wave * 16 < R;
-  Vec16 qf[D / CH];
+  Vec16 qf[D / CH];  // the B operand of S^T
   {
     const int hh = r / a.bs, j = r % a.bs;
     const T *qp = reinterpret_cast<const T *>(a.q) +
@@ -64,6 +67,11 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int dc = 0; dc < D / CH; ++dc) qf[dc] = rvalid ? load_vec16(qp + dc * CH) : zero_vec16();
   }
+  for (int i = threadIdx.x; i < npg; i += 256) pgs[i] = bt[min(pbeg + i, a.maxb - 1)];
+  __syncthreads();
+  const int T_total = c + a.bs;
+  if (kbeg >= T_total) return;  // nothing for this split (uniform over the work-group)
+  const int kend = min(T_total, kbeg + a.chunk);
 
   f32x4_t acc_o[D / 16];
 #pragma unroll
@@ -75,45 +83,30 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
   const T *vc = reinterpret_cast<const T *>(a.vc);
   const T *kbk = reinterpret_cast<const T *>(a.kb);
   const T *vbk = reinterpret_cast<const T *>(a.vb);
-  const int32_t *bt = a.block_table + (size_t)b * a.maxb;
 
   // Staging of a 64-key tile. K: item v = (key v / CPR, 16-byte part v % CPR), one row-major
   // vector write each. V is stored transposed (vts[d][key]) by items of two consecutive keys
   // (2 kappa, 2 kappa + 1) and one part: the pair of values of each d goes out as one 4-byte
   // (bf16) or 8-byte (fp32) write. Within a wave, 16 consecutive kappa x 4 parts write each
   // row, so a write instruction touches at most two rows that share banks.
-  // The loads of tile t + 1 are in registers while tile t is computed, and the page-table
-  // entries they need are read a tile earlier still: page reads depend only on the key index
-  // (clamped into the table), never on the context length.
   constexpr int KVEC = kTileKeys * CPR / 256;  // K items per thread
   constexpr int VVEC = (kTileKeys / 2) * CPR / 256;  // V items per thread
   static_assert(kTileKeys * CPR % 256 == 0 && (kTileKeys / 2) * CPR % 256 == 0, "staging items per thread");
   auto v_kappa = [](int v) { return (v & 15) | (((v >> 6) & 1) << 4); };
   auto v_part = [](int v) { return ((v >> 4) & 3) | ((v >> 7) << 2); };
-  int kpg[KVEC], vpg[VVEC][2];
   struct TileRegs {
     Vec16 k[KVEC], v[VVEC][2];
   };
   TileRegs ra, rb;  // two tiles' loads in flight: tile n in ra (n even) or rb (n odd)
-  auto load_pages = [&](int t0) {
-#pragma unroll
-    for (int i = 0; i < KVEC; ++i) {
-      const int t = t0 + ((int)threadIdx.x + i * 256) / CPR;
-      kpg[i] = bt[min(t / a.P, a.maxb - 1)];
-    }
-#pragma unroll
-    for (int i = 0; i < VVEC; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = t0 + 2 * v_kappa((int)threadIdx.x + i * 256) + h;
-        vpg[i][h] = bt[min(t / a.P, a.maxb - 1)];
-      }
-  };
-  // source of key t (part `part`) in the context cache or the block's own k / v
-  auto key_off = [&](int t, int page, int part, bool &ctx) {
-    ctx = t < c;
-    if (ctx) return ((size_t)(min(max(page, 0), a.num_pages - 1) * a.P + t % a.P) * a.KVH + g) * D + part * KPV;
-    return ((size_t)(b * a.bs + (t - c)) * a.KVH + g) * D + part * KPV;
+  // Source of key t (16-byte part `part`): the context cache (page from the LDS table) or the
+  // block's own k / v. Both addresses are formed (each in range for any t of the split) and the
+  // pointer selected, with no branch.
+  auto key_src = [&](const T *cache, const T *blk, int t, int part) -> const T * {
+    const int page = min(max(pgs[t / a.P - pbeg], 0), a.num_pages - 1);
+    const size_t coff = ((size_t)(page * a.P + t % a.P) * a.KVH + g) * D + part * KPV;
+    const size_t boff = ((size_t)(b * a.bs + max(t - c, 0)) * a.KVH + g) * D + part * KPV;
+    const T *pc = cache + coff, *pb = blk + boff;
+    return t < c ? pc : pb;
   };
   // Keys past kend read key kend - 1 (in range; the scores mask them and their V rows are
   // finite, so they add nothing): every load is unconditional, with no select on its value
@@ -122,9 +115,7 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KVEC; ++i) {
       const int v = threadIdx.x + i * 256, t = min(t0 + v / CPR, kend - 1);
-      bool ctx;
-      const size_t off = key_off(t, kpg[i], v % CPR, ctx);
-      rr.k[i] = load_vec16((ctx ? kc : kbk) + off);
+      rr.k[i] = load_vec16(key_src(kc, kbk, t, v % CPR));
     }
 #pragma unroll
     for (int i = 0; i < VVEC; ++i) {
@@ -132,22 +123,16 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int t = min(t0 + 2 * v_kappa(v) + h, kend - 1);
-        bool ctx;
-        const size_t off = key_off(t, vpg[i][h], v_part(v), ctx);
-        rr.v[i][h] = load_vec16((ctx ? vc : vbk) + off);
+        rr.v[i][h] = load_vec16(key_src(vc, vbk, t, v_part(v)));
       }
     }
   };
-  // Tile n's loads go out two tiles ahead (while tiles n - 2 and n - 1 compute); the page
-  // reads a tile ahead of those.
+  // Tile n's loads go out two tiles ahead, while tiles n - 2 and n - 1 compute. The issues are
+  // unconditional (past the last tile they read key kend - 1 again, an L2 hit): a conditional
+  // one makes the compiler wait for every load in flight where the paths meet.
   const int ntiles = (kend - kbeg + kTileKeys - 1) / kTileKeys;
-  load_pages(kbeg);
   issue(ra, kbeg);
-  if (ntiles > 1) {
-    load_pages(kbeg + kTileKeys);
-    issue(rb, kbeg + kTileKeys);
-  }
-  if (ntiles > 2) load_pages(kbeg + 2 * kTileKeys);
+  issue(rb, kbeg + kTileKeys);
 
   auto tile = [&](TileRegs &rr, int n) {
     const int t0 = kbeg + n * kTileKeys;
@@ -176,10 +161,7 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
     }
     __syncthreads();
     // ---- tile n + 2's loads into the registers just written out
-    if (n + 2 < ntiles) {
-      issue(rr, t0 + 2 * kTileKeys);
-      if (n + 3 < ntiles) load_pages(t0 + 3 * kTileKeys);
-    }
+    issue(rr, t0 + 2 * kTileKeys);
     if (wave * 16 >= R) return;
 
     // ---- S^T tiles: 4 tiles of 16 keys; tile sb row rho holds key
@@ -301,14 +283,16 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
 
 // Online log-sum-exp accumulation of up to 16 split partials (m, l, o) into a running
 // (m_acc, l_acc, o_acc) of one output element, in split order: the loads of all 16 are issued
-// before any is used, so one round trip covers 16 splits.
+// before any is used, so one round trip covers 16 splits. The load addresses are clamped to
+// the nmax splits of the workspace, not to the sequence's ns, so that the first loads need
+// not wait for the sequence length; splits at or past ns are never used.
 __device__ __forceinline__ void merge16(const float *pm, const float *pl, const float *po, size_t stride_ml,
-                                        size_t stride_o, int s0, int step, int ns, float &m_acc, float &l_acc,
-                                        float &o_acc) {
+                                        size_t stride_o, int s0, int step, int ns, int nmax, float &m_acc,
+                                        float &l_acc, float &o_acc) {
   float mv[16], lv[16], pv[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
-    const int q = min(s0 + u * step, ns - 1);
+    const int q = min(s0 + u * step, nmax - 1);
     mv[u] = pm[(size_t)q * stride_ml];
     lv[u] = pl[(size_t)q * stride_ml];
     pv[u] = po[(size_t)q * stride_o];
@@ -341,10 +325,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   if (row >= a.bs * G) return;
   const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
-  if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel
   const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64 + row;
   float m = -INFINITY, l = 0.f, o = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 16) merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, 1, ns, m, l, o);
+  int s0 = 0;  // the first 16 splits' loads go out with the length's
+  do merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, 1, ns, a.nsplit, m, l, o);
+  while ((s0 += 16) < ns);
+  if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel
   const int hh = row / a.bs, j = row % a.bs;
   a.o[((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d] = o / l;
 }
@@ -362,11 +348,12 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(AttnArgs a) {
   const int d = threadIdx.x % D, sub = threadIdx.x / D;
   const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
-  if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel
   const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64 + row;
   float m = -INFINITY, l = 0.f, o = 0.f;
-  for (int s0 = sub; s0 < ns; s0 += 16 * nsub)
-    merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, nsub, ns, m, l, o);
+  int s0 = sub;  // the first loads go out with the length's (a sub with no split adds nothing)
+  do merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, nsub, ns, a.nsplit, m, l, o);
+  while ((s0 += 16 * nsub) < ns);
+  if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel (uniform)
   so[threadIdx.x] = o;
   if (d == 0) {
     sm[sub] = m;
@@ -423,6 +410,8 @@ __global__ __launch_bounds__(256) void attn_items_kernel(AttnArgs a, int *items,
 
 template <typename T>
 hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
+  // the partial kernel keeps a split's page-table entries in LDS and pipelines whole tiles
+  if (a.chunk < kTileKeys || a.chunk > kMaxChunk || a.chunk % kTileKeys || a.P < 1) return hipErrorInvalidValue;
   dim3 grid = a.items ? dim3(a.nsplit * a.KVH * a.B) : dim3(a.nsplit, a.KVH, a.B);
   {
     ProfScope prof("attn_partial", s);
@@ -447,13 +436,15 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 }  // namespace
 
 void attn_plan(int B, int KVH, int max_keys, int *chunk, int *nsplit) {
-  // Aim for ~768 work-groups in total (a round and a half at two per CU), in splits of at least one
-  // 64-key tile and at most eight: with many sequences of unequal length, short splits keep
-  // the work-groups even.
-  long want = (long)max_keys * B * KVH / 768;
+  // Two work-groups fit on a CU. One sequence: at most about 512 work-groups (one round, so no
+  // work-group of a long context waits for a slot), in splits of up to sixteen 64-key tiles.
+  // Several: about 768 (a round and a half), in splits of one to eight tiles: with many
+  // sequences of unequal length, short splits keep the work-groups even.
+  const long target = B == 1 ? 512 : 768;
+  long want = ((long)max_keys * B * KVH + target - 1) / target;
   int ch = (int)((want + kTileKeys - 1) / kTileKeys) * kTileKeys;
   if (ch < kTileKeys) ch = kTileKeys;
-  if (ch > 8 * kTileKeys) ch = 8 * kTileKeys;
+  if (ch > (B == 1 ? kMaxChunk : kMaxChunk / 2)) ch = B == 1 ? kMaxChunk : kMaxChunk / 2;
   *chunk = ch;
   *nsplit = (max_keys + ch - 1) / ch;
 }
