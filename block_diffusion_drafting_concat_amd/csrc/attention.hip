@@ -437,13 +437,14 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 
 void attn_plan(int B, int KVH, int max_keys, int *chunk, int *nsplit) {
   // Two work-groups fit on a CU. One sequence: at most about 512 work-groups (one round, so no
-  // work-group of a long context waits for a slot), in splits of up to sixteen 64-key tiles.
-  // Several: about 768 (a round and a half), in splits of one to eight tiles: with many
-  // sequences of unequal length, short splits keep the work-groups even.
+  // work-group of a long context waits for a slot), in splits of two to sixteen 64-key tiles
+  // (at 2048 keys, two-tile splits beat one-tile ones: the second tile costs less than the
+  // merge of twice the partials). Several: about 768 (a round and a half), in splits of one to
+  // eight tiles: with many sequences of unequal length, short splits keep the work-groups even.
   const long target = B == 1 ? 512 : 768;
   long want = ((long)max_keys * B * KVH + target - 1) / target;
   int ch = (int)((want + kTileKeys - 1) / kTileKeys) * kTileKeys;
-  if (ch < kTileKeys) ch = kTileKeys;
+  if (ch < (B == 1 ? 2 : 1) * kTileKeys) ch = (B == 1 ? 2 : 1) * kTileKeys;
   if (ch > (B == 1 ? kMaxChunk : kMaxChunk / 2)) ch = B == 1 ? kMaxChunk : kMaxChunk / 2;
   *chunk = ch;
   *nsplit = (max_keys + ch - 1) / ch;
