@@ -129,8 +129,12 @@ def load_traffic(kernel: str, workload: str):
 
 # ---------------------------------------------------------------------------------------------
 class Bench:
-    def __init__(self, wl: synth.Workload):
+    def __init__(self, wl: synth.Workload, forked: bool = False):
         self.wl, self.spec = wl, wl.spec
+        # forked: the step's injection runs on a second stream (default priority) and the
+        # proposal waits for it only before its first attention
+        self.forked = forked
+        self.side, self.injected = torch.cuda.Stream(), torch.cuda.Event()
         spec = self.spec
         t0 = time.time()
         self.W = synth.make_weights(spec, wl.seed)
@@ -217,8 +221,16 @@ class Bench:
         inject the context rows, propose one block, verify it (acceptance counters fused)."""
         seq, pos, slots, bonus = binding.prepare(self.prev_out, self.spec.vocab, self.opt_seq, self.row_req,
                                                  self.opt_pos, self.bt_dev, self.layout.page_size, out=self.prep)
-        self.dev.inject(self.cache, self.step_aux, pos, slots, self.ws_inj)
-        self.dev.propose(self.cache, bonus, seq, self.max_ctx, self.ws_prop, out=self.out)
+        if self.forked:
+            self.side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(self.side):
+                self.dev.inject(self.cache, self.step_aux, pos, slots, self.ws_inj)
+                self.injected.record()
+            self.dev.propose(self.cache, bonus, seq, self.max_ctx, self.ws_prop, out=self.out,
+                             cache_ready=self.injected)
+        else:
+            self.dev.inject(self.cache, self.step_aux, pos, slots, self.ws_inj)
+            self.dev.propose(self.cache, bonus, seq, self.max_ctx, self.ws_prop, out=self.out)
         binding.verify_with_stats(self.out[1], self.target, self.stats, out=self.vout)
 
     def timed(self, steps):
@@ -316,6 +328,9 @@ def main():
                     help="also run one 1 GiB device copy (scale reference for rocprofv3 byte counters)")
     ap.add_argument("--eager", action="store_true",
                     help="report eager launches instead of replays of the captured step graph")
+    ap.add_argument("--fork-inject", action="store_true",
+                    help="run the step's injection on a second stream, overlapping the proposal's embedding and "
+                         "first QKV projection (dflash_propose_block_after); measured no faster on MI355X")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the drafting path of this build is "
@@ -327,7 +342,7 @@ def main():
     torch.cuda.set_device(0)
     wl = synth.WORKLOADS[args.workload]
     spec = wl.spec
-    bench = Bench(wl)
+    bench = Bench(wl, forked=args.fork_inject)
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
@@ -476,7 +491,8 @@ def main():
                    "context": [int(wl.ctx_lo), int(wl.ctx_hi)], "inject_rows_per_seq": wl.inject_rows,
                    "hidden": spec.hidden, "layers": spec.n_layers, "heads": [spec.n_q_heads, spec.n_kv_heads],
                    "head_dim": spec.head_dim, "intermediate": spec.intermediate, "vocab": spec.vocab,
-                   "fc_in": spec.n_aux * spec.target_hidden, "page_size": wl.page_size},
+                   "fc_in": spec.n_aux * spec.target_hidden, "page_size": wl.page_size,
+                   "injection": "forked onto a second stream" if bench.forked else "serial"},
         "draft_blocks_per_s": B / sec_best,
         "timing": timing,
         "ms_per_step_loop": sec_loop * 1e3,

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
                                                _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dflash_propose_block.argtypes = [P(Config), P(Weights), P(KvCache), _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                            _vp, ctypes.c_size_t, _vp]
+        L.dflash_propose_block_after.argtypes = [P(Config), P(Weights), P(KvCache), _i32, _vp, _vp, _i32, _vp, _vp,
+                                                 _vp, _vp, ctypes.c_size_t, _vp, _vp]
         L.dflash_propose_block_noalloc.argtypes = [P(Config), P(Weights), P(KvCache), _i32, _vp, _vp, _i32, _vp, _vp,
                                                    _vp, _vp]
         L.dflash_greedy_verify.argtypes = [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -77,7 +79,8 @@ def lib() -> ctypes.CDLL:
         L.dflash_prepare_proposal_inputs.argtypes = [_i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32,
                                                      _vp, _vp, _vp, _vp, _vp]
         for fn in ("dflash_build_rope_table", "dflash_build_fused_kv_weight", "dflash_inject_context_kv",
-                   "dflash_propose_block", "dflash_propose_block_noalloc", "dflash_greedy_verify",
+                   "dflash_propose_block", "dflash_propose_block_after", "dflash_propose_block_noalloc",
+                   "dflash_greedy_verify",
                    "dflash_greedy_verify_stats", "dflash_prepare_proposal_inputs"):
             getattr(L, fn).restype = _i32
         L.dflash_profile_enable.argtypes = [_i32]
@@ -152,6 +155,16 @@ def propose_block(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, dra
                                       _ptr(bonus_tokens), _ptr(seq_lens), max_context, _ptr(draft_token_ids),
                                       _ptr(drafts_only), _ptr(hidden_out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def propose_block_after(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, draft_token_ids, drafts_only,
+                        hidden_out, workspace, cache_ready=None, stream=None) -> None:
+    """`cache_ready`: a torch.cuda.Event recorded after the step's injection (or None)."""
+    ev = cache_ready.cuda_event if cache_ready is not None else None
+    _check(lib().dflash_propose_block_after(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), batch,
+                                            _ptr(bonus_tokens), _ptr(seq_lens), max_context, _ptr(draft_token_ids),
+                                            _ptr(drafts_only), _ptr(hidden_out), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), ev, _stream(stream)))
 
 
 def propose_block_noalloc(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, draft_token_ids, drafts_only,
@@ -250,14 +263,18 @@ class Drafter:
                           stream)
 
     def propose(self, cache: PagedCache, bonus, seq_lens, max_context: int, workspace, out=None,
-                hidden_out=None, stream=None):
+                hidden_out=None, stream=None, cache_ready=None):
         B = int(bonus.shape[0])
         K = self.spec.block_size - 1
         if out is None:
             out = (torch.empty((B, K + 1), dtype=torch.int32, device=bonus.device),
                    torch.empty((B, K), dtype=torch.int32, device=bonus.device))
-        propose_block(self.cfg, self.struct, cache.struct, B, bonus, seq_lens, max_context, out[0], out[1],
-                      hidden_out, workspace, stream)
+        if cache_ready is None:
+            propose_block(self.cfg, self.struct, cache.struct, B, bonus, seq_lens, max_context, out[0], out[1],
+                          hidden_out, workspace, stream)
+        else:
+            propose_block_after(self.cfg, self.struct, cache.struct, B, bonus, seq_lens, max_context, out[0], out[1],
+                                hidden_out, workspace, cache_ready, stream)
         return out
 
     def propose_noalloc(self, cache: PagedCache, bonus, seq_lens, max_context: int, out=None, hidden_out=None,

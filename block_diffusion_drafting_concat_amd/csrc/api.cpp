@@ -447,9 +447,16 @@ dflash_status propose_check(const dflash_config *cfg, const dflash_weights *w, c
 dflash_status propose_enqueue(const dflash_config *cfg, const dflash_weights *w, const dflash_kv_cache *cache,
                               int32_t batch, const int32_t *bonus_tokens, const int32_t *seq_lens,
                               int32_t max_context, int32_t *draft_token_ids, int32_t *drafts_only, float *hidden_out,
-                              void *workspace, const ProposePlan &p, void *stream) {
+                              void *workspace, const ProposePlan &p, void *stream, void *cache_ready = nullptr) {
   const int L = cfg->n_layers;
   hipStream_t s = (hipStream_t)stream;
+  // the first launch that reads the cache waits for `cache_ready` (when given)
+  bool waited = cache_ready == nullptr;
+  auto wait_cache = [&]() -> hipError_t {
+    if (waited) return hipSuccess;
+    waited = true;
+    return hipStreamWaitEvent(s, (hipEvent_t)cache_ready, 0);
+  };
   const bool bf = is_bf16(cfg);
   const int H = cfg->hidden, D = cfg->head_dim, QH = cfg->n_q_heads, KVH = cfg->n_kv_heads;
   const int I = cfg->intermediate, bs = cfg->block_size, K = bs - 1, M = p.M;
@@ -516,6 +523,7 @@ dflash_status propose_enqueue(const dflash_config *cfg, const dflash_weights *w,
     pa.sync = ctr + p.n_ctr;
     pa.ws = workspace, pa.ws_bytes = (unsigned)p.total;
     plk_abort = pa.sync + p.plk.sync_words - 1;
+    HIP_TRY(wait_cache());
     HIP_TRY(launch_plk(pa, s));
     ss_groups = H / 128;
   }
@@ -564,6 +572,7 @@ dflash_status propose_enqueue(const dflash_config *cfg, const dflash_weights *w,
     at_.pm = at<float>(workspace, p.off_pm);
     at_.pl = at<float>(workspace, p.off_pl);
     at_.o = o;
+    HIP_TRY(wait_cache());
     if (batch > 1) {
       // the work-groups that have keys, listed once for every layer (same sequence lengths)
       int *items = at<int>(workspace, p.off_items), *n_items = items + (size_t)batch * KVH * p.nsplit;
@@ -617,6 +626,7 @@ dflash_status propose_enqueue(const dflash_config *cfg, const dflash_weights *w,
   HIP_TRY(launch_gemm(gl, bf, GemmEpi::kArgmax, p.lm, s));
   HIP_TRY(launch_argmax_reduce(batch, K, p.lm.col_groups, gl.amax_val, gl.amax_idx, bonus_tokens, cfg->vocab,
                                plk_abort, draft_token_ids, drafts_only, s));
+  HIP_TRY(wait_cache());  // no layer read the cache: the call still ends after the event
   return ok();
 }
 
@@ -662,6 +672,22 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
   if (!workspace) return fail(DFLASH_ERR_INVALID_ARGUMENT, "workspace is NULL");
   return propose_enqueue(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, draft_token_ids, drafts_only,
                          hidden_out, workspace, p, stream);
+}
+
+dflash_status dflash_propose_block_after(const dflash_config *cfg, const dflash_weights *w,
+                                         const dflash_kv_cache *cache, int32_t batch, const int32_t *bonus_tokens,
+                                         const int32_t *seq_lens, int32_t max_context, int32_t *draft_token_ids,
+                                         int32_t *drafts_only, float *hidden_out, void *workspace,
+                                         size_t workspace_bytes, void *cache_ready, void *stream) {
+  ProposePlan p{};
+  bool nothing = false;
+  dflash_status st = propose_check(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, draft_token_ids,
+                                   drafts_only, workspace_bytes, &p, &nothing);
+  if (st != DFLASH_OK) return st;
+  if (nothing) return ok();
+  if (!workspace) return fail(DFLASH_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  return propose_enqueue(cfg, w, cache, batch, bonus_tokens, seq_lens, max_context, draft_token_ids, drafts_only,
+                         hidden_out, workspace, p, stream, cache_ready);
 }
 
 dflash_status dflash_propose_block_noalloc(const dflash_config *cfg, const dflash_weights *w,

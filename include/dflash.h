@@ -190,6 +190,24 @@ dflash_status dflash_propose_block(const dflash_config *cfg, const dflash_weight
                                    int32_t *drafts_only, float *hidden_out, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/* Block proposal overlapped with the step's injection ([N] "Context KV Injection" and
+ * "DFlashProposer": the injected rows are context for the block that follows). The same
+ * computation, arguments, outputs and errors as dflash_propose_block, plus `cache_ready`: a
+ * hipEvent_t (NULL: none), recorded by the caller after the injection of this step's rows,
+ * on any stream of the same device. The embedding and the first layer's QKV projection read
+ * no cache and are enqueued first; the stream waits for the event before the first launch
+ * that reads the cache (the first layer's attention; with no layer, after the last launch),
+ * so an injection running on another stream overlaps with them, and the proposal's completion
+ * on `stream` implies the event's. The two calls must use different workspaces. The event is
+ * only waited on, never recorded or destroyed; under stream capture it must be recorded in
+ * the same capture. */
+dflash_status dflash_propose_block_after(const dflash_config *cfg, const dflash_weights *w,
+                                         const dflash_kv_cache *cache, int32_t batch,
+                                         const int32_t *bonus_tokens, const int32_t *seq_lens,
+                                         int32_t max_context, int32_t *draft_token_ids,
+                                         int32_t *drafts_only, float *hidden_out, void *workspace,
+                                         size_t workspace_bytes, void *cache_ready, void *stream);
+
 /* Bytes of the static device scratch that dflash_propose_block_noalloc uses (per GPU). */
 #define DFLASH_STATIC_SCRATCH_BYTES (64u << 20)
 

@@ -2,7 +2,9 @@
 hipGraph and replayed: every replay, with eager work of the same library in between, must
 reproduce the eager step bit for bit (drafts, verification, cache rows, counters). The library
 enqueues kernels only (no allocation, memset or host synchronisation), which is what makes the
-step capturable."""
+step capturable. The forked step runs the injection on a second stream and the proposal with
+dflash_propose_block_after, which waits for the injection's event only before the first
+attention: eager and replayed, it must give the serial step's results bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -17,11 +19,13 @@ SPEC = synth.DrafterSpec(hidden=256, n_layers=2, n_q_heads=8, n_kv_heads=2, head
                          rope_theta=1e6, dtype="bf16")
 
 
+@pytest.mark.parametrize("forked", [False, True])
 @pytest.mark.parametrize("ctx,acc", [([300, 77, 150], [1, SPEC.block_size, 6]),
                                      ([300], [6]),  # one sequence: one row tile per projection
                                      # 96 block rows: the tiled GEMM, its split-K counters
                                      ([300, 77, 150, 40, 200, 90], [1, SPEC.block_size, 6, 3, 9, 2])])
-def test_captured_step_replays_match_the_eager_step(ctx, acc):
+def test_captured_step_replays_match_the_eager_step(ctx, acc, forked):
+    print(f"\n[case] graph ctx={ctx} forked={forked}", flush=True)
     ctx = np.array(ctx, np.int32)
     st = Setup(SPEC, ctx, seed=3)
     B, K, n = st.B, SPEC.block_size - 1, 8
@@ -49,10 +53,19 @@ def test_captured_step_replays_match_the_eager_step(ctx, acc):
     stats = torch.zeros(3, dtype=torch.int64, device="cuda")
     ws_inj = st.dev.workspace(binding.DFLASH_OP_INJECT, B * n)
 
-    def step():
+    side, injected = torch.cuda.Stream(), torch.cuda.Event()
+
+    def step(fork=False):
         seq, pos, slots, bonus = binding.prepare(prev_d, SPEC.vocab, opt_seq_d, req_d, opt_pos_d, bt_d, st.P, out=prep)
-        st.dev.inject(st.cache, aux_d, pos, slots, ws_inj)
-        st.dev.propose(st.cache, bonus, seq, st.max_ctx, st.ws_prop, out=out)
+        if fork:  # injection on the side stream, overlapping the embedding and the first QKV
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                st.dev.inject(st.cache, aux_d, pos, slots, ws_inj)
+                injected.record()
+            st.dev.propose(st.cache, bonus, seq, st.max_ctx, st.ws_prop, out=out, cache_ready=injected)
+        else:
+            st.dev.inject(st.cache, aux_d, pos, slots, ws_inj)
+            st.dev.propose(st.cache, bonus, seq, st.max_ctx, st.ws_prop, out=out)
         binding.verify_with_stats(out[1], target, stats, out=vout)
 
     step()
@@ -61,10 +74,17 @@ def test_captured_step_replays_match_the_eager_step(ctx, acc):
     ref_rows = [gpu_cache_rows(st, b, np.arange(int(ctx[b]) - n, int(ctx[b]))) for b in range(B)]
     assert np.array_equal(prep[0].cpu().numpy(), ctx) and np.array_equal(prep[1].cpu().numpy(), true_pos)
     per_step = stats.clone()
+    if forked:  # the forked eager step gives the serial step's results
+        for t in (*prep, *out, *vout):
+            t.fill_(-7)
+        step(fork=True)
+        torch.cuda.synchronize()
+        for got, want in zip((*prep, *out, *vout), ref):
+            assert torch.equal(got, want)
 
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        step()
+        step(fork=forked)
     torch.cuda.synchronize()
     stats.zero_()
     other = (torch.empty((B, K + 1), dtype=torch.int32, device="cuda"),
