@@ -637,8 +637,8 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
 //      planes (17 significant bits of each value) once, not once per column tile (the LM
 //      head takes the hi plane alone, see gemm_plan); the weight and activation tiles then go
 //      through registers into LDS, the loads of two steps in flight while a step's MFMAs run.
-//      The LDS tiles hold 16-row blocks of 32 bf16 chunk-major (tile_off), so that both the
-//      fragment reads and the stores of the loaded rows run at the LDS's full rate. The tile then
+//      The LDS tiles are [rows][32] bf16 with the 16-byte chunks of a row XOR-swizzled by
+//      (row / 4) % 4, so the 16 rows of a fragment read fall on distinct banks. The tile then
 //      goes through LDS to the epilogue in two halves (fp32 store / residual add with per-tile
 //      row sums of squares, SwiGLU, per-tile argmax, the head epilogues), which keeps a
 //      work-group at 48 KiB of LDS: three fit on a CU. With fewer tiles than CUs, or to keep a
@@ -659,18 +659,7 @@ template <int BM, int BN> struct TileLds {
   }
 };
 
-// LDS offset of 16-byte chunk c (8 bf16 of K) of tile row `row`. A 16-row block takes 1 KiB,
-// chunk-major: 256 bytes per chunk, the rows of each 8-row half in their own 128 bytes, XOR-
-// permuted by 2c there. Measured on gfx950 (bank-conflict counters of single-wave probes): a
-// 16-byte read instruction takes 4 cycles when each 8-lane group reads one 128-byte half of a
-// 256-byte window and the two groups of a 16-lane quarter the two halves, 8 otherwise (any
-// row-major tile of 64-byte rows, swizzled or padded); a 16-byte write takes 8 cycles when the
-// 8 lanes of each group hit distinct 16-byte slots modulo 128 bytes. The fragment read (lane
-// reads row lane % 16, chunk lane / 16) meets the first; the store (lane holds row lane / 4,
-// chunk lane % 4: rows 2k, 2k+1 per 8 lanes, their slots (r % 8) ^ 2c distinct) the second.
-__device__ __forceinline__ int tile_off(int row, int c) {
-  return (row >> 4) * 1024 + 256 * c + 128 * ((row >> 3) & 1) + 16 * ((row & 7) ^ (2 * c));
-}
+__device__ __forceinline__ int tile_swz(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
 
 // The activations of the tiled GEMM, once per launch: row m of A (the kept rows of the block
 // for the LM head), normalised when the GEMM norms on load (also written to a_out), split into
@@ -742,7 +731,8 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
   const int kseg = K / g.a_nseg;                // bf16 A: K columns per segment
   // Loads of one K step, per thread: JA 16-byte chunks of activation rows (hi and lo each)
   // and JW of weight rows; chunk slot j of wave w is tile row (4 j + w) * 16 + lane / 4. Tile
-  // row r's chunk c (c = lane % 4 of the loading thread) is stored at tile_off(r, c).
+  // row r's chunk c is stored at tile_swz(r, c); thread slot (row, stored chunk lane % 4)
+  // holds source chunk (lane % 4) ^ swz(row).
   const uint16_t *brow[JW], *ahi[JA], *alo[JA];
   size_t aoff[JA];
   int bsrc[JW], asrc[JA];
@@ -755,12 +745,12 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
     if (!kDual)
       while (seg < g.b_nseg - 1 && n >= g.b_end[seg]) nbase = g.b_end[seg++];
     brow[j] = reinterpret_cast<const uint16_t *>(kDual ? g.b[r < OC ? 0 : 1] : g.b[seg]) + (size_t)(n - nbase) * K;
-    bsrc[j] = (lane & 3) * 8;
+    bsrc[j] = ((lane & 3) ^ ((r >> 2) & 3)) * 8;
   }
 #pragma unroll
   for (int j = 0; j < JA; ++j) {
     const int r = (j * 4 + wave) * 16 + (lane >> 2);
-    asrc[j] = (lane & 3) * 8;
+    asrc[j] = ((lane & 3) ^ ((r >> 2) & 3)) * 8;
     const int am = min(m0 + r, g.M - 1);  // rows past M: a valid row, never stored
     aoff[j] = (size_t)am * (kLo ? (size_t)K : (size_t)g.lda);
     ahi[j] = reinterpret_cast<const uint16_t *>(g.a[0]) + aoff[j];
@@ -790,14 +780,13 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
   auto store = [&](int set, int buf) {
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
-      const int o = tile_off((j * 4 + wave) * 16 + (lane >> 2), lane & 3);
+      const int o = (j * 4 + wave) * 1024 + lane * 16;
       *reinterpret_cast<uint4 *>(smem + buf * kTileABytes + o) = aregs[set][0][j].u;
       if constexpr (kLo) *reinterpret_cast<uint4 *>(smem + buf * kTileABytes + BM * BK * 2 + o) = aregs[set][1][j].u;
     }
 #pragma unroll
     for (int j = 0; j < JW; ++j)
-      *reinterpret_cast<uint4 *>(smem + kTileW + buf * kTileWBytes + tile_off((j * 4 + wave) * 16 + (lane >> 2), lane & 3)) =
-          wregs[set][j].u;
+      *reinterpret_cast<uint4 *>(smem + kTileW + buf * kTileWBytes + (j * 4 + wave) * 1024 + lane * 16) = wregs[set][j].u;
   };
   // vmcnt(NLD): the newest step's loads may stay in flight
   static_assert(NLD <= 15, "vmcnt field");
@@ -825,10 +814,10 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
     const unsigned char *sw = smem + kTileW + set * kTileWBytes;
     Vec16 bf[UN];
 #pragma unroll
-    for (int u = 0; u < UN; ++u) bf[u].u = *reinterpret_cast<const uint4 *>(sw + tile_off(wn * WN + u * 16 + (lane & 15), lane >> 4));
+    for (int u = 0; u < UN; ++u) bf[u].u = *reinterpret_cast<const uint4 *>(sw + tile_swz(wn * WN + u * 16 + (lane & 15), lane >> 4));
 #pragma unroll
     for (int t = 0; t < TF; ++t) {
-      const int o = tile_off(wm * WM + t * 16 + (lane & 15), lane >> 4);
+      const int o = tile_swz(wm * WM + t * 16 + (lane & 15), lane >> 4);
       Vec16 ah, al;
       ah.u = *reinterpret_cast<const uint4 *>(sa + o);
       if constexpr (kLo) al.u = *reinterpret_cast<const uint4 *>(sa + BM * BK * 2 + o);
