@@ -26,6 +26,8 @@ namespace dflash {
 namespace {
 
 constexpr int kTileKeys = 64;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kMaxChunk = 16 * kTileKeys;  // keys per split at most (attn_plan)
 
 template <typename T, int D>
@@ -98,41 +100,42 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
     Vec16 k[KVEC], v[VVEC][2];
   };
   TileRegs ra, rb;  // two tiles' loads in flight: tile n in ra (n even) or rb (n odd)
-  // Source of key t (16-byte part `part`): the context cache (page from the LDS table) or the
-  // block's own k / v. Both addresses are formed (each in range for any t of the split) and the
-  // pointer selected, with no branch.
-  auto key_src = [&](const T *cache, const T *blk, int t, int part) -> const T * {
-    const int page = min(max(pgs[t / a.P - pbeg], 0), a.num_pages - 1);
-    const size_t coff = ((size_t)(page * a.P + t % a.P) * a.KVH + g) * D + part * KPV;
-    const size_t boff = ((size_t)(b * a.bs + max(t - c, 0)) * a.KVH + g) * D + part * KPV;
-    const T *pc = cache + coff, *pb = blk + boff;
-    return t < c ? pc : pb;
-  };
-  // Keys past kend read key kend - 1 (in range; the scores mask them and their V rows are
-  // finite, so they add nothing): every load is unconditional, with no select on its value
-  // before the LDS write, so none waits for another.
-  auto issue = [&](TileRegs &rr, int t0) {
+  // Loads of a tile, two tiles ahead. Each lane first forms the source row of key t0 + lane
+  // (one page lookup per lane and tile): r >= 0 is a slot of the context cache, r < 0 the
+  // block's own row -1 - r. Every staging item then takes its key's row from the owning lane
+  // (a cross-lane read) and forms its address with no division and no branch. Past the last
+  // tile the issues read the last tile again (L2 hits); keys past kend in the last tile are
+  // block keys, clamped to the block's last row, and are masked in the scores.
+  auto issue = [&](TileRegs &rr, int t0, int tlast) {
+    int row;
+    {
+      const int t = min(t0, tlast) + lane;
+      const int page = min(max(pgs[t / a.P - pbeg], 0), a.num_pages - 1);
+      row = t < c ? page * a.P + t % a.P : -1 - (b * a.bs + min(t - c, a.bs - 1));
+    }
+    auto src = [&](const T *cache, const T *blk, int kk, int part) -> const T * {
+      const int r = __shfl(row, kk, 64);
+      const size_t off = ((size_t)(unsigned)(r ^ (r >> 31)) * a.KVH + g) * D + part * KPV;  // row r or -1 - r
+      return (r >= 0 ? cache : blk) + off;
+    };
 #pragma unroll
     for (int i = 0; i < KVEC; ++i) {
-      const int v = threadIdx.x + i * 256, t = min(t0 + v / CPR, kend - 1);
-      rr.k[i] = load_vec16(key_src(kc, kbk, t, v % CPR));
+      const int v = threadIdx.x + i * 256;
+      rr.k[i] = load_vec16(src(kc, kbk, v / CPR, v % CPR));
     }
 #pragma unroll
     for (int i = 0; i < VVEC; ++i) {
       const int v = threadIdx.x + i * 256;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = min(t0 + 2 * v_kappa(v) + h, kend - 1);
-        rr.v[i][h] = load_vec16(key_src(vc, vbk, t, v_part(v)));
-      }
+      for (int h = 0; h < 2; ++h) rr.v[i][h] = load_vec16(src(vc, vbk, 2 * v_kappa(v) + h, v_part(v)));
     }
   };
   // Tile n's loads go out two tiles ahead, while tiles n - 2 and n - 1 compute. The issues are
   // unconditional (past the last tile they read key kend - 1 again, an L2 hit): a conditional
   // one makes the compiler wait for every load in flight where the paths meet.
-  const int ntiles = (kend - kbeg + kTileKeys - 1) / kTileKeys;
-  issue(ra, kbeg);
-  issue(rb, kbeg + kTileKeys);
+  const int ntiles = (kend - kbeg + kTileKeys - 1) / kTileKeys, tlast = kbeg + (ntiles - 1) * kTileKeys;
+  issue(ra, kbeg, tlast);
+  issue(rb, kbeg + kTileKeys, tlast);
 
   auto tile = [&](TileRegs &rr, int n) {
     const int t0 = kbeg + n * kTileKeys;
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
     }
     __syncthreads();
     // ---- tile n + 2's loads into the registers just written out
-    issue(rr, t0 + 2 * kTileKeys);
+    issue(rr, t0 + 2 * kTileKeys, tlast);
     if (wave * 16 >= R) return;
 
     // ---- S^T tiles: 4 tiles of 16 keys; tile sb row rho holds key
@@ -191,8 +194,10 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // m_new is finite (every computed tile has a key below kend), so the raw exponential needs
+    // no guard: the first tile's alpha (m_run = -inf) and masked keys' p (-inf) come out 0
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
@@ -201,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
     for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = (s[sb][i] == -INFINITY) ? 0.f : exp2f(s[sb][i] - m_new);
+        const float p = __builtin_amdgcn_exp2f(s[sb][i] - m_new);
         s[sb][i] = p;
         l_run += p;
       }
@@ -210,12 +215,16 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int ps = 0; ps < 4 / NB; ++ps) {
       if constexpr (KPV == 8) {
-        uint16_t hi[8], lo[8];
+        // hi = bf16(p), lo = bf16(p - hi), two values per conversion instruction (RNE)
+        uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = s[ps * 2 + e / 4][e % 4];
-          hi[e] = f32_to_bf16(p);
-          lo[e] = f32_to_bf16(p - bf16_to_f32(hi[e]));
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = s[ps * 2 + e / 2][(2 * e) % 4], p1 = s[ps * 2 + e / 2][(2 * e + 1) % 4];
+          const bf16x2_t h = __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t);
+          __builtin_memcpy(&hi[e], &h, 4);
+          const float h0 = __uint_as_float(hi[e] << 16), h1 = __uint_as_float(hi[e] & 0xffff0000u);
+          const bf16x2_t l = __builtin_convertvector(f32x2_t{p0 - h0, p1 - h1}, bf16x2_t);
+          __builtin_memcpy(&lo[e], &l, 4);
         }
         Vec16 phi, plo;
         __builtin_memcpy(&phi.u, hi, 16);
