@@ -293,8 +293,7 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
 // Online log-sum-exp accumulation of up to 16 split partials (m, l, o) into a running
 // (m_acc, l_acc, o_acc) of one output element, in split order: the loads of all 16 are issued
 // before any is used, so one round trip covers 16 splits. The load addresses are clamped to
-// the nmax splits of the workspace, not to the sequence's ns, so that the first loads need
-// not wait for the sequence length; splits at or past ns are never used.
+// nmax (>= ns) splits; splits at or past ns are loaded but never used.
 __device__ __forceinline__ void merge16(const float *pm, const float *pl, const float *po, size_t stride_ml,
                                         size_t stride_o, int s0, int step, int ns, int nmax, float &m_acc,
                                         float &l_acc, float &o_acc) {
@@ -336,8 +335,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
   const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64 + row;
   float m = -INFINITY, l = 0.f, o = 0.f;
-  int s0 = 0;  // the first 16 splits' loads go out with the length's
-  do merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, 1, ns, a.nsplit, m, l, o);
+  // One sequence: the first 16 splits' loads go out with the length's (clamped to the
+  // workspace's splits). Several: only the sequence's own splits are read.
+  const int nmax = a.B == 1 ? a.nsplit : ns;
+  int s0 = 0;
+  do merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, 1, ns, nmax, m, l, o);
   while ((s0 += 16) < ns);
   if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel
   const int hh = row / a.bs, j = row % a.bs;
@@ -359,8 +361,10 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(AttnArgs a) {
   const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
   const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64 + row;
   float m = -INFINITY, l = 0.f, o = 0.f;
-  int s0 = sub;  // the first loads go out with the length's (a sub with no split adds nothing)
-  do merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, nsub, ns, a.nsplit, m, l, o);
+  // as in attn_merge_kernel (a sub with no split adds nothing)
+  const int nmax = a.B == 1 ? a.nsplit : ns;
+  int s0 = sub;
+  do merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, nsub, ns, nmax, m, l, o);
   while ((s0 += 16 * nsub) < ns);
   if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel (uniform)
   so[threadIdx.x] = o;
