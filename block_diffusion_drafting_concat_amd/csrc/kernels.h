@@ -167,11 +167,12 @@ hipError_t launch_attention_items(const AttnArgs &a, int *items, int *n_items, h
 // Persistent layer-stack kernel for one block of at most 16 rows (batch 1), bf16 drafters with
 // head_dim 128: every layer's QKV, attention, split merge, O, gate|up and down projections run
 // as jobs of one launch with one work-group per CU. Each work-group has four compute waves
-// (weights -> MFMA, the next chunk's weights always in flight), a stager wave (waits for the
-// producer tiles a job reads, stages its activations in LDS) and a finisher wave (split-K
-// partials, the last contributor's reduction and epilogue, readiness flags). A job waits only
-// for the producer tiles that cover its K range; the RMSNorm row scale of a normalised GEMM
-// input is applied in the reducer's epilogue, so no phase needs a grid-wide barrier.
+// (weights -> MFMA, the next two jobs' weights always in flight), three stager waves (wait for
+// the producer tiles a job reads, stage its activations in LDS with the RMSNorm row scale
+// applied, stage attention tiles, merge attention splits) and a finisher wave (split-K
+// partials, the last contributor's reduction and epilogue, readiness flags, attention tiles).
+// The waves hand off through LDS words; work-groups through device-scope flags and counters.
+// Every wait is bounded; a work-group that gives up raises an abort word, and the drafts are -1.
 // ------------------------------------------------------------------------------------------
 constexpr int kPlkMaxLayers = 8;
 
