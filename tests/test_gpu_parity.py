@@ -61,6 +61,12 @@ def _compare_cache(spec, st, kc, vc, seqs):
     # every sequence within one 64-key attention split: normalised in place, no merge launch
     (SMALL_BF16, [0, 20, 3, 40], 16, True),
     (SMALL_BF16_LONG_MLP, [5, 90, 0, 33, 70], 16, True),
+    # page sizes that do not divide a 64-key tile, and one larger than a tile (the per-lane page
+    # lookup of the attention's K/V loads); one sequence in many splits (the row-parallel merge)
+    (SMALL_BF16, [77, 300, 5], 7, True),
+    (SMALL_BF16, [1000], 48, True),
+    (SMALL_BF16, [700, 33], 128, True),
+    (SMALL_BF16, [4000], 16, True),
 ])
 def test_inject_and_propose_match_oracle(spec, ctx, P, shuffle):
     print(f"\n[case] spec={spec.dtype} H={spec.hidden} ctx={ctx} P={P}", flush=True)
