@@ -243,6 +243,35 @@ class Bench:
 
 
 # ---------------------------------------------------------------------------------------------
+def microbench() -> dict:
+    """Attainable rates on this GPU, for context beside the published peaks the rooflines use:
+    a 1 GiB device-to-device copy (read + written bytes / time) and a library bf16 GEMM
+    (8192^3, fp32 accumulation). Medians of 5 event-timed repetitions after one untimed."""
+    def timed(fn):
+        fn()
+        ms = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return float(np.median(ms))
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = timed(lambda: dst.copy_(src))
+    del src, dst
+    n = 8192
+    x = torch.randn(n, n, device="cuda").to(torch.bfloat16).contiguous()
+    y = torch.randn(n, n, device="cuda").to(torch.bfloat16).contiguous()
+    gemm_ms = timed(lambda: torch.matmul(x, y))
+    del x, y
+    return {"copy_GBs": 2 * (1 << 30) / (copy_ms * 1e6), "bf16_gemm_TFs": 2.0 * n ** 3 / (gemm_ms * 1e9),
+            "note": "attainable rates for context (1 GiB device copy: read + write bytes; torch.matmul bf16 "
+                    "8192^3); the rooflines use the published peaks"}
+
+
 def timing_loop_name(sec_graph, sec_plain) -> str:
     return "replays of the captured step graph" if sec_graph and sec_graph <= sec_plain else "eager launches (no events)"
 
@@ -439,6 +468,7 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+    micro = microbench()
 
     # the faster of the two ways of running the same step: replays of the captured graph, or
     # eager launches with no event (both enqueue the identical kernels)
@@ -504,6 +534,7 @@ def main():
         "step_ms_distribution": step_dist,
         "step_ms_distribution_mall_evicted": step_dist_evicted,
         "mall_eviction_effect": step_dist_evicted["p50"] / step_dist["p50"] - 1.0,
+        "microbench": micro,
         "step_timing_note": "distributions: hipEvents around each " + ("graph replay" if sec_graph else "eager step")
                             + "; the evicted run fills a 512 MiB buffer (twice the 256 MiB MALL) before each "
                               "step, outside the timed pair",
