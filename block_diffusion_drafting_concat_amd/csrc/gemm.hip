@@ -664,7 +664,8 @@ __device__ __forceinline__ int tile_swz(int row, int c) { return row * 64 + ((c 
 // The activations of the tiled GEMM, once per launch: row m of A (the kept rows of the block
 // for the LM head), normalised when the GEMM norms on load (also written to a_out), split into
 // two bf16 planes hi [M][K] = bf16(f) and lo [M][K] = bf16(f - hi): hi + lo is the fp32
-// value f to 17 significant bits (relative error at most 2^-17).
+// value f to 17 significant bits (relative error at most 2^-17). lo == nullptr: the hi plane
+// alone (a GEMM that takes bf16(f)).
 __global__ __launch_bounds__(256) void split_rows_kernel(GemmArgs g, uint16_t *__restrict__ hi,
                                                          uint16_t *__restrict__ lo) {
   __shared__ float red[16];
@@ -700,7 +701,7 @@ __global__ __launch_bounds__(256) void split_rows_kernel(GemmArgs g, uint16_t *_
       l[e] = f32_to_bf16(f[e] - bf16_to_f32(h[e]));
     }
     __builtin_memcpy(hi + (size_t)m * K + k, h, 16);
-    __builtin_memcpy(lo + (size_t)m * K + k, l, 16);
+    if (lo) __builtin_memcpy(lo + (size_t)m * K + k, l, 16);
   }
 }
 
@@ -978,7 +979,7 @@ hipError_t launch_tiled_shape(const GemmArgs &g, const GemmPlan &p, hipStream_t 
   GemmArgs t = g;
   if constexpr (kLo) {
     uint16_t *hi = g.a_split, *lo = g.a_split + (size_t)g.M * g.K;
-    split_rows_kernel<<<g.M, 256, 0, s>>>(g, hi, lo);
+    split_rows_kernel<<<g.M, 256, 0, s>>>(g, hi, p.hi_only ? nullptr : lo);
     t.a[0] = hi;
     t.a[1] = lo;
     t.a_nseg = 1;
@@ -1143,11 +1144,13 @@ GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bo
     // one work-group per CU: a second one on a CU shares its LDS and matrix cores and adds
     // little) per unit of work, plus a small cost per extra split for the reduction through
     // the workspace; at least 32 K steps per split.
-    // The LM head's fp32 input rows enter the matrix cores as one bf16 plane (not a hi + lo
-    // pair): half the MFMAs and half the A tile. A CPU study on the batch-128 workload (every
-    // GEMM input rounded to bf16 in turn) changed no draft whose top-2 logit gap is >= 1e-2 when
-    // the LM head's input was rounded.
-    p.hi_only = a_f32 && epi == GemmEpi::kArgmax;
+    // The fp32 input rows of the LM head and of gate|up enter the matrix cores as one bf16
+    // plane (not a hi + lo pair): half the MFMAs and half the A tile. A CPU study on the
+    // batch-128 workload (GEMM inputs rounded to bf16, one projection or a set at a time)
+    // changed no draft whose top-2 logit gap is >= 1e-2 when the LM head's and gate|up's inputs
+    // were rounded together (0 of 839 such drafts over four samples of 24 sequences); rounding
+    // the QKV, O or down inputs as well did change some.
+    p.hi_only = a_f32 && (epi == GemmEpi::kArgmax || epi == GemmEpi::kSwiGLU);
     const long wgs = (long)p.col_groups * p.row_blocks, slots = cu_count();
     p.splits = smin;
     if (smin == 1 && wgs < slots) {

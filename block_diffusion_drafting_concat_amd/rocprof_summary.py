@@ -49,6 +49,8 @@ def short_name(name: str) -> str:
     if m:
         return (f"gemm_tiled_kernel<{EPI[m.group(1)]},{'hi+lo-A' if m.group(2) == 'true' else 'bf16-A'},"
                 f"{m.group(3)}x{m.group(4)}>")
+    if name.startswith("Cijk_"):  # a library GEMM kernel (bench.py's attainable-rate check)
+        return "library bf16 GEMM (" + name.split("_MT")[1].split("_")[0] + " tiles)" if "_MT" in name else name[:40]
     name = re.sub(r"^void ", "", name)
     name = name.replace("dflash::(anonymous namespace)::", "")
     return re.sub(r"\(.*$", "", name)

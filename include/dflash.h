@@ -20,10 +20,11 @@
  *    states and KV caches use the config's storage dtype: bfloat16 (raw 16-bit bf16 values)
  *    or fp32. Activations stay fp32 inside the library; a bf16 GEMM takes each fp32
  *    activation f as two bf16 values, hi = bf16(f) and lo = bf16(f - hi), whose sum keeps 17
- *    significant bits of f (relative error at most 2^-17, about 7.6e-6), except the LM head of
- *    a proposal with more than 64 kept rows, which takes hi alone (bf16(f), relative error at
- *    most 2^-9). The block's q/k/v are rounded to the storage type like cached K/V. The RoPE table and hidden_out are
- *    fp32. Token ids and positions are int32; slots are int64.
+ *    significant bits of f (relative error at most 2^-17, about 7.6e-6), except the LM head
+ *    and the gate|up projection of a proposal with more than 64 block rows, which take hi
+ *    alone (bf16(f), relative error at most 2^-9). The block's q/k/v are rounded to the
+ *    storage type like cached K/V. The RoPE table and hidden_out are fp32. Token ids and
+ *    positions are int32; slots are int64.
  *  - Host-side validation covers pointers and scalars only. A call that fails validation
  *    (DFLASH_ERR_INVALID_ARGUMENT, DFLASH_ERR_UNSUPPORTED, DFLASH_ERR_WORKSPACE_TOO_SMALL)
  *    returns before enqueuing anything; every chunk and workspace carve-up of the call is
