@@ -23,6 +23,13 @@ SMALL_BF16_LONG_MLP = synth.DrafterSpec(hidden=256, n_layers=1, n_q_heads=8, n_k
 SMALL_BF16_D64 = synth.DrafterSpec(hidden=384, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64,
                                    intermediate=384, vocab=1008, n_aux=4, target_hidden=96, block_size=8,
                                    mask_token_id=1007, rope_theta=1e4, dtype="bf16")
+# hidden 1024, intermediate 14336, vocabulary 32016: with 20 sequences (320 block rows, 300
+# kept) gate|up (2 x 112 column tiles) and the LM head (2 x 126) take the wide 256 x 256 tile,
+# with a ragged last row tile and a ragged last vocabulary tile (16 columns)
+WIDE_TILE_BF16 = synth.DrafterSpec(hidden=1024, n_layers=1, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                   intermediate=14336, vocab=32016, n_aux=2, target_hidden=192, block_size=16,
+                                   mask_token_id=32015, rope_theta=1e6, dtype="bf16")
+WIDE_TILE_CTX = [0, 5, 64, 130, 3, 40, 1, 257, 17, 90, 33, 0, 12, 200, 64, 7, 100, 29, 300, 2]
 
 
 def _compare_drafts(spec, got_ids, got_drafts, ref, bonus, what):
@@ -67,6 +74,7 @@ def _compare_cache(spec, st, kc, vc, seqs):
     (SMALL_BF16, [1000], 48, True),
     (SMALL_BF16, [700, 33], 128, True),
     (SMALL_BF16, [4000], 16, True),
+    (WIDE_TILE_BF16, WIDE_TILE_CTX, 16, True),
 ])
 def test_inject_and_propose_match_oracle(spec, ctx, P, shuffle):
     print(f"\n[case] spec={spec.dtype} H={spec.hidden} ctx={ctx} P={P}", flush=True)

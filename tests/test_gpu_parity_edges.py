@@ -10,7 +10,7 @@ promises:
   * the greedy argmax's lowest-index tie rule ([N] "DFlash Draft Model Architecture", greedy
     sampling) on the GPU, with a drafted token's LM-head row duplicated to a lower and a higher
     vocabulary index, in one small case and in the full vocabulary where the copies land in
-    other work-groups;
+    other work-groups, and with many rows where they land in other wide tiles;
   * NaN-poisoned workspaces, caches (outside the contexts) and outputs.
 
 Every call goes through the C ABI; the oracle recomputes what each call must write."""
@@ -21,6 +21,7 @@ import torch
 from block_diffusion_drafting_concat_amd import binding, synth
 from oracle import dflash_oracle as O
 from tests.gpu_helpers import Setup, check_close, lazy_numpy, mode_of
+from tests.test_gpu_parity import WIDE_TILE_BF16, WIDE_TILE_CTX
 
 pytestmark = pytest.mark.gpu
 
@@ -194,6 +195,13 @@ def _tie_case(st, what, far):
 def test_argmax_tie_rule_small():
     st = Setup(SMALL_BF16, [40], seed=5)
     _tie_case(st, "small vocab 2048", far=300)
+
+
+def test_argmax_tie_rule_wide_tiles():
+    """20 sequences, 300 kept rows: the LM head takes the 256 x 256 wide tile; copies 10000
+    columns apart land in different column tiles, merged by the argmax reduction."""
+    st = Setup(WIDE_TILE_BF16, WIDE_TILE_CTX, shuffle=True, seed=5)
+    _tie_case(st, "wide tiles, vocab 32016", far=10000)
 
 
 def test_argmax_tie_rule_full_vocab(c2):
