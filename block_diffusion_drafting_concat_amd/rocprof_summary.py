@@ -35,8 +35,8 @@ def source_sha(paths=GEMM_SOURCES) -> str:
 
 def short_name(name: str) -> str:
     """'gemm_kernel<unsigned short, 1, 8, 1, 1, 8, (dflash::GemmEpi)3, false, true>(...)' ->
-    'gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=1,NCG=8,kArgmax,fp32-A>'; other kernels: the name
-    without arguments."""
+    'gemm_kernel<bf16,MT=1,CW=8,CT=1,KW=1,NCG=8,kArgmax,fp32-A>'; the tiled and wide GEMMs
+    likewise; other kernels: the name without arguments."""
     m = re.search(r"gemm_kernel<([^,]+), (\d+), (\d+), (\d+), (\d+), (\d+), \(dflash::GemmEpi\)(\d), "
                   r"(true|false), (true|false)>", name)
     if m:
@@ -49,6 +49,9 @@ def short_name(name: str) -> str:
     if m:
         return (f"gemm_tiled_kernel<{EPI[m.group(1)]},{'hi+lo-A' if m.group(2) == 'true' else 'bf16-A'},"
                 f"{m.group(3)}x{m.group(4)}>")
+    m = re.search(r"gemm_wide_kernel<\(dflash::GemmEpi\)(\d)(?:, (true|false))?>", name)
+    if m:
+        return f"gemm_wide_kernel<{EPI[m.group(1)]},{'hi+lo-A' if m.group(2) == 'true' else 'bf16-A'},256x256>"
     if name.startswith("Cijk_"):  # a library GEMM kernel (bench.py's attainable-rate check)
         return "library bf16 GEMM (" + name.split("_MT")[1].split("_")[0] + " tiles)" if "_MT" in name else name[:40]
     name = re.sub(r"^void ", "", name)
