@@ -52,7 +52,7 @@ TILED_KERNELS = {
     "gemm_tiled_kernel<kResidAdd,hi+lo-A> (down)": ("gemm.down",),
     "gemm_wide_kernel<kSwiGLU,bf16-A,256x256> or gemm_tiled_kernel<kSwiGLU,bf16-A> (gate_up)": ("gemm.gate_up",),
     "gemm_wide_kernel<kArgmax,bf16-A,256x256> or gemm_tiled_kernel<kArgmax,bf16-A> (lm_head)": ("gemm.lm_head",),
-    "gemm_tiled_kernel<kStore,bf16-A> (fc)": ("gemm.fc",),
+    "gemm_wide_kernel<kStore,bf16-A,256x256> or gemm_tiled_kernel<kStore,bf16-A> (fc)": ("gemm.fc",),
     "gemm_tiled_kernel<kKvScatter,hi+lo-A> (kv)": ("gemm.kv",),
 }
 GEMM_SOURCES = ("block_diffusion_drafting_concat_amd/csrc/gemm.hip", "block_diffusion_drafting_concat_amd/csrc/common.h")

@@ -968,26 +968,30 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
   }
 }
 
-// ---- Wide tiles, one work-group per CU: a 256 x 256 tile of a projection whose A is the bf16
-//      plane alone (the LM head and gate|up with many rows). Eight waves (4 x 2) of 64 x 128
-//      with v_mfma_f32_32x32x16_bf16 (128 accumulators per lane), two waves per SIMD; K in
-//      steps of 32 with three steps in flight (register sets and LDS buffers, XOR-swizzled
+// ---- Wide tiles, one work-group per CU: a 256 x 256 output tile. Eight waves (4 x 2) of
+//      64 x 128 with v_mfma_f32_32x32x16_bf16 (128 accumulators per lane), two waves per SIMD;
+//      K in steps of 32 with three steps in flight (register sets and LDS buffers, XOR-swizzled
 //      row-major tiles as above). A work-group loads 2.5 times fewer bytes per flop than a
 //      64 x 256 tile, which is what bounds the smaller tile: its loads at full MFMA rate would
-//      exceed what a CU's vector-memory path delivers. The tile then goes through LDS in four
-//      pieces of 64 rows to the SwiGLU or per-tile argmax epilogue. No K split: the plan takes
-//      this tile only when there are about as many tiles as CUs or more.
+//      exceed what a CU's vector-memory path delivers. A is either the bf16 plane of fp32 rows
+//      (the LM head and gate|up with many rows; never K-split) or bf16 rows read in place in
+//      K segments (fc over the auxiliary target states; with fewer tiles than CUs, K is split
+//      over work-groups and the last split of a tile reduces, as in the tiled kernel). The tile
+//      then goes through LDS in four pieces of 64 rows to the SwiGLU, per-tile argmax or store
+//      (with per-tile row sums of squares) epilogue.
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-constexpr int kWideM = 256, kWideN = 256, kWideWaves = 8, kWideStages = 3, kWidePiece = 64;
+constexpr int kWideM = 256, kWideN = 256, kWideWaves = 8, kWidePiece = 64;
+constexpr int kWideStages = 3;
 constexpr size_t kWideLds = (size_t)kWideStages * (kWideM + kWideN) * kTileK * 2;
 
-template <GemmEpi E>
-__global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs g, int mtiles, int ntiles) {
-  static_assert(E == GemmEpi::kSwiGLU || E == GemmEpi::kArgmax, "wide tile epilogues");
+template <GemmEpi E, bool kSeg>
+__global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs g, int mtiles, int ntiles, int nsplit) {
+  static_assert(kSeg ? E == GemmEpi::kStore : (E == GemmEpi::kSwiGLU || E == GemmEpi::kArgmax), "wide tile epilogues");
   constexpr int BM = kWideM, BN = kWideN, BK = kTileK, NS = kWideStages, HM = kWidePiece;
   constexpr int NT = kWideWaves * 64, NW = kWideWaves, WR = 4, WC = 2;
   constexpr int WM = BM / WR, WN = BN / WC, TF = WM / 32, UN = WN / 32;  // 32 x 32 MFMA tiles per wave
-  constexpr int JA = BM * 4 / NT, JW = BN * 4 / NT, NLD = JA + JW;     // 16-byte loads per thread and step
+  constexpr int JA = BM * 4 / NT, JW = BN * 4 / NT;                  // 16-byte loads per thread, plane and step
+  constexpr int NLD = JA + JW;
   static_assert(JA * NT == BM * 4 && JW * NT == BN * 4 && HM == WM, "one epilogue piece per wave row");
   constexpr size_t kAB = (size_t)BM * BK * 2, kWB = (size_t)BN * BK * 2;
   static_assert((size_t)HM * (BN + 4) * 4 <= kWideLds, "epilogue piece fits the K-loop buffers");
@@ -995,21 +999,24 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
   constexpr int OC = kDual ? BN / 2 : BN;  // output columns of a tile (SwiGLU: BN/2 gate + BN/2 up rows)
   constexpr int FS = BN + 4, TPR = NT / HM;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ unsigned s_flag;
+  const int splits = kSeg ? nsplit : 1;  // the bf16-plane tiles are never split
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WC, wn = wave % WC;
-  // work-group -> (column tile, row tile): the row tiles of a column tile run back to back on
-  // one XCD (ids congruent mod 8), sharing the weight tile through its L2
+  // work-group -> (column tile, row tile, K split): the row tiles and splits of a column tile run
+  // back to back on one XCD (ids congruent mod 8), sharing the weight tile through its L2
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int nt = (slot / mtiles) * 8 + xcd, mt = slot % mtiles;
+  const int nt = (slot / (mtiles * splits)) * 8 + xcd, mt = slot % mtiles, sp = (slot / mtiles) % splits;
   if (nt >= ntiles) return;
   const int m0 = mt * BM, n0 = nt * OC, K = g.K;
   // load slot j of wave w: tile row (NW j + w) * 16 + lane / 4, stored chunk lane % 4, which
   // holds source chunk (lane % 4) ^ swz(row)
-  const uint16_t *arow[JA], *brow[JW];
+  size_t aoff[JA];
+  const uint16_t *brow[JW];
 #pragma unroll
   for (int j = 0; j < JA; ++j) {
     const int r = (j * NW + wave) * 16 + (lane >> 2);
-    arow[j] = reinterpret_cast<const uint16_t *>(g.a[0]) + (size_t)min(m0 + r, g.M - 1) * K +
-              ((lane & 3) ^ ((r >> 2) & 3)) * 8;  // rows past M: a valid row, never stored
+    // rows past M: a valid row, never stored
+    aoff[j] = (size_t)min(m0 + r, g.M - 1) * (kSeg ? (size_t)g.lda : (size_t)K) + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
   }
 #pragma unroll
   for (int j = 0; j < JW; ++j) {
@@ -1018,10 +1025,19 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
     brow[j] = reinterpret_cast<const uint16_t *>(g.b[kDual && r >= OC ? 1 : 0]) + (size_t)n * K +
               ((lane & 3) ^ ((r >> 2) & 3)) * 8;
   }
+  const uint16_t *ahi = reinterpret_cast<const uint16_t *>(g.a[0]);
   Vec16 areg[NS][JA], wreg[NS][JW];
+  const int kseg = K / g.a_nseg;  // bf16 A in segments: K columns per segment
   auto load = [&](int set, int k0) {
+    if constexpr (kSeg) {  // the segment of the concatenated A holding columns [k0, k0 + BK)
+      const int seg = k0 / kseg;
+      const uint16_t *a0 = reinterpret_cast<const uint16_t *>(g.a[seg]) + (k0 - seg * kseg);
 #pragma unroll
-    for (int j = 0; j < JA; ++j) areg[set][j] = load_vec16(arow[j] + k0);
+      for (int j = 0; j < JA; ++j) areg[set][j] = load_vec16(a0 + aoff[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < JA; ++j) areg[set][j] = load_vec16(ahi + aoff[j] + k0);
+    }
 #pragma unroll
     for (int j = 0; j < JW; ++j) wreg[set][j] = load_vec16(brow[j] + k0);
   };
@@ -1040,8 +1056,9 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
   for (int t = 0; t < TF; ++t)
 #pragma unroll
     for (int u = 0; u < UN; ++u) acc[t][u] = f32x16_t{};
-  const int nk = K / BK;
-  auto kof = [&](int step) { return min(step, nk - 1) * BK; };  // past the end: the last step again
+  // this split's K steps [ks0, ks0 + nk) of the K / BK (splits of near-equal length)
+  const int ks0 = (int)((long)sp * (K / BK) / splits), nk = (int)((long)(sp + 1) * (K / BK) / splits) - ks0;
+  auto kof = [&](int step) { return (ks0 + min(step, nk - 1)) * BK; };  // past the end: the last step again
 #pragma unroll
   for (int q = 0; q < NS; ++q) load(q, kof(q));
   __builtin_amdgcn_s_waitcnt(kWaitOlder);  // step 0 has landed, the next NS - 1 in flight
@@ -1088,12 +1105,11 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
   if (ks + 1 < nk) step(std::integral_constant<int, 1>{}, ks + 1);
   __builtin_amdgcn_s_waitcnt(0);  // the clamped loads past the end
 
-  // ---- epilogue, one piece of 64 rows at a time: piece h is held by the waves with wm == h.
-  //      32 x 32 MFMA layout: lane holds column lane % 32, rows 8 (i / 4) + 4 (lane / 32) + i % 4.
+  // ---- the tile through LDS, one piece of 64 rows at a time: piece h is held by the waves
+  //      with wm == h. 32 x 32 MFMA layout: lane holds column lane % 32, rows
+  //      8 (i / 4) + 4 (lane / 32) + i % 4.
   float *fin = reinterpret_cast<float *>(smem);
-  for (int h = 0; h < BM / HM; ++h) {
-    const int mh = m0 + h * HM;  // first output row of this piece
-    __syncthreads();             // the previous piece (or the K loop) is done with the LDS
+  auto acc_to_fin = [&](int h) {
     if (wm == h)
 #pragma unroll
       for (int t = 0; t < TF; ++t)
@@ -1102,9 +1118,77 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             fin[(t * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3)) * FS + wn * WN + u * 32 + (lane & 31)] = acc[t][u][i];
+  };
+  // ---- split-K: every split stores its tile ([split][row tile][column tile] blocks of
+  //      BM x BN in the workspace) and the last to arrive sums all splits in split order, with
+  //      the device-scope relaxed atomic accesses and store-complete-before-arrival protocol of
+  //      the streaming kernel.
+  const size_t tstride = (size_t)mtiles * ntiles * BM * BN;
+  const size_t tbase = ((size_t)mt * ntiles + nt) * BM * BN;
+  if (splits > 1) {
+    float *mine = g.part + (size_t)sp * tstride + tbase;
+    for (int h = 0; h < BM / HM; ++h) {
+      __syncthreads();
+      acc_to_fin(h);
+      __syncthreads();
+      for (int e = threadIdx.x; e < HM * BN; e += NT)
+        __hip_atomic_store(mine + h * HM * BN + e, fin[(e / BN) * FS + e % BN], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
+    __syncthreads();
+    unsigned *ctr = g.counters + (size_t)mt * ntiles + nt;
+    if (threadIdx.x == 0) s_flag = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_flag != (unsigned)(splits - 1)) return;  // another split finishes this tile
+    if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  for (int h = 0; h < BM / HM; ++h) {
+    const int mh = m0 + h * HM;  // first output row of this piece
+    __syncthreads();             // the previous piece (or the K loop) is done with the LDS
+    if (splits > 1) {
+      for (int e = threadIdx.x; e < HM * BN; e += NT) {
+        const float *src = g.part + tbase + h * HM * BN + e;
+        float sum = 0.f;
+        for (int q0 = 0; q0 < splits; q0 += 4) {  // loads of 4 splits in flight, summed in split order
+          float v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            v[u] = q0 + u < splits ? __hip_atomic_load(src + (size_t)(q0 + u) * tstride, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0.f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (q0 + u < splits) sum += v[u];
+        }
+        fin[(e / BN) * FS + e % BN] = sum;
+      }
+    } else {
+      acc_to_fin(h);
+    }
     __syncthreads();
     if (mh >= g.M) break;  // rows past M: nothing to store (uniform)
-    if constexpr (E == GemmEpi::kSwiGLU) {
+    if constexpr (E == GemmEpi::kStore) {
+      for (int e = threadIdx.x; e < HM * BN; e += NT) {
+        const int row = e / BN, col = e % BN, m = mh + row, n = n0 + col;
+        float v = fin[row * FS + col];
+        if (m < g.M && n < g.N) {
+          g.out[(size_t)m * g.N + n] = v;
+        } else {
+          v = 0.f;
+        }
+        fin[row * FS + col] = v * v;
+      }
+      if (g.ss_out) {  // per-row sum of squares over this column tile, for norm on load
+        __syncthreads();
+        const int row = threadIdx.x / TPR, sub = threadIdx.x % TPR;
+        float sq = 0.f;
+        for (int c = sub; c < BN; c += TPR) sq += fin[row * FS + c];
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) sq += __shfl_xor(sq, o, 64);
+        if (sub == 0 && mh + row < g.M) g.ss_out[(size_t)nt * g.M + mh + row] = sq;
+      }
+    } else if constexpr (E == GemmEpi::kSwiGLU) {
       for (int e = threadIdx.x; e < HM * OC; e += NT) {
         const int row = e / OC, col = e % OC, m = mh + row, n = n0 + col;
         if (m < g.M && n < g.N) {
@@ -1132,13 +1216,24 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
   }
 }
 
+// bf16 A in segments (fc over the auxiliary target states), read in place
+hipError_t launch_wide_seg(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
+  auto kern = gemm_wide_kernel<GemmEpi::kStore, true>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds);
+  if (attr != hipSuccess) return attr;
+  const int ntiles = p.col_groups, mtiles = p.row_blocks;
+  kern<<<(ntiles + 7) / 8 * 8 * mtiles * p.splits, kWideWaves * 64, kWideLds, s>>>(g, mtiles, ntiles, p.splits);
+  return hipGetLastError();
+}
+
 // the fp32 rows as their bf16 plane (norm on load), then the wide-tile kernel
 template <GemmEpi E>
 hipError_t launch_wide(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
   if constexpr (E != GemmEpi::kSwiGLU && E != GemmEpi::kArgmax) {
     return hipErrorInvalidValue;
   } else {
-    auto kern = gemm_wide_kernel<E>;
+    auto kern = gemm_wide_kernel<E, false>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds);
     if (attr != hipSuccess) return attr;
@@ -1149,7 +1244,7 @@ hipError_t launch_wide(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
     t.a_nseg = 1;
     t.lda = g.K;
     const int ntiles = p.col_groups, mtiles = p.row_blocks;
-    kern<<<(ntiles + 7) / 8 * 8 * mtiles, kWideWaves * 64, kWideLds, s>>>(t, mtiles, ntiles);
+    kern<<<(ntiles + 7) / 8 * 8 * mtiles, kWideWaves * 64, kWideLds, s>>>(t, mtiles, ntiles, 1);
     return hipGetLastError();
   }
 }
@@ -1188,7 +1283,12 @@ hipError_t launch_tiled_shape(const GemmArgs &g, const GemmPlan &p, hipStream_t 
 
 template <GemmEpi E, bool kLo>
 hipError_t launch_tiled(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
-  if (p.tile_m == kWideM) return launch_wide<E>(g, p, s);
+  if (p.tile_m == kWideM) {  // the bf16 plane of fp32 rows (SwiGLU, argmax), or fc's bf16 segments
+    if constexpr (E == GemmEpi::kStore && !kLo)
+      return launch_wide_seg(g, p, s);
+    else
+      return launch_wide<E>(g, p, s);
+  }
   return p.tile_n == 256 ? launch_tiled_shape<E, kLo, 64, 256>(g, p, s) : launch_tiled_shape<E, kLo, 128, 128>(g, p, s);
 }
 
@@ -1354,6 +1454,21 @@ GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bo
         if (cost < best - 1e-9) best = cost, p.splits = s;
       }
     }
+    // fc (bf16 rows in K segments, more than one wide row tile) takes the wide tile too, K split
+    // toward one round of work-groups (at least 64 K steps a split): batch 128 0.41 -> 0.29 ms,
+    // batch 32 0.47 -> 0.40 ms per step
+    if (!a_f32 && epi == GemmEpi::kStore && M > kWideM && K / kTileK >= 64) {
+      p.tile_n = kWideN;
+      p.tile_m = kWideM;
+      p.col_groups = (N + p.tile_n - 1) / p.tile_n;
+      p.row_blocks = (M + p.tile_m - 1) / p.tile_m;
+      const long tiles = (long)p.col_groups * p.row_blocks;
+      double best = 1e30;
+      for (int s = 1; s <= 8 && 64 * s <= K / kTileK; ++s) {
+        const double cost = (double)((tiles * s + slots - 1) / slots) / s + 0.03 * (s - 1);
+        if (cost < best - 1e-9) best = cost, p.splits = s;
+      }
+    }
     return p;
   }
   const bool head = epi == GemmEpi::kHeadNormRope || epi == GemmEpi::kKvScatter;
@@ -1413,7 +1528,8 @@ hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, const GemmPla
         p.row_blocks != (g0.M + p.tile_m - 1) / p.tile_m || !((p.tile_m == 128 && p.tile_n == 128) ||
         (p.tile_m == 64 && p.tile_n == 256) ||
         (p.tile_m == kWideM && p.tile_n == kWideN && p.hi_only && p.splits == 1 && g0.a_f32 &&
-         (epi == GemmEpi::kSwiGLU || (epi == GemmEpi::kArgmax && g0.b_nseg == 1)))) || g0.b_nseg < 1 || g0.b_nseg > 3 || p.splits < 1 ||
+         (epi == GemmEpi::kSwiGLU || (epi == GemmEpi::kArgmax && g0.b_nseg == 1))) ||
+        (p.tile_m == kWideM && p.tile_n == kWideN && !g0.a_f32 && epi == GemmEpi::kStore && g0.b_nseg == 1)) || g0.b_nseg < 1 || g0.b_nseg > 3 || p.splits < 1 ||
         p.splits > g0.K / kTileK || (p.splits > 1 && (!g0.part || !g0.counters)) ||
         (head && ((g0.head_dim != 64 && g0.head_dim != 128) || g0.N % g0.head_dim)))
       return hipErrorInvalidValue;

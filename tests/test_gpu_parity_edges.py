@@ -214,6 +214,7 @@ def test_argmax_tie_rule_full_vocab(c2):
     (SMALL_BF16, [300]),                          # batch 1: streaming GEMMs, split attention
     (SMALL_BF16, [0, 5, 64, 257, 33, 130]),       # 96 rows: tiled GEMMs, merges, one empty context
     (TINY, [0, 37, 200]),
+    (WIDE_TILE_BF16, WIDE_TILE_CTX),              # gate|up and the LM head on the wide tile
 ])
 def test_nan_poisoned_workspace_cache_and_outputs(spec, ctx):
     """Workspaces (0xFF bytes: NaN and all-ones counters), every cache slot outside the
