@@ -83,11 +83,17 @@ int main() {
   std::vector<const void *> aux(c.n_aux, dummy(0x600000));
   const int32_t *pos = static_cast<const int32_t *>(dummy(0x700000));
   const int64_t *slots = static_cast<const int64_t *>(dummy(0x800000));
-  // workspace too small for some chunk of a multi-chunk injection: refused before any launch
+  // workspace too small for a chunk of an injection (one chunk or several): refused before any
+  // launch (a launch here, with no device, would return a HIP error instead). The query is the
+  // maximum over every chunk size up to its row count, so a call can need less than it: the
+  // workspaces below are too small for any chunk of these calls.
+  const size_t need16 = dflash_workspace_bytes(&c, DFLASH_OP_INJECT, 16, 0);
   for (int rows : {16, 4096, 4196, 12289}) {
-    const size_t need = dflash_workspace_bytes(&c, DFLASH_OP_INJECT, rows, 0);
-    CHECK(dflash_inject_context_kv(&c, &w, &cache, aux.data(), 4096, rows, pos, slots, dummy(0x900000), need / 2,
-                                   nullptr) == DFLASH_ERR_WORKSPACE_TOO_SMALL);
+    for (size_t ws : {(size_t)1, need16}) {
+      if (rows <= 16 && ws == need16) continue;  // enough for a 16-row call
+      CHECK(dflash_inject_context_kv(&c, &w, &cache, aux.data(), 4096, rows, pos, slots, dummy(0x900000), ws,
+                                     nullptr) == DFLASH_ERR_WORKSPACE_TOO_SMALL);
+    }
   }
   CHECK(dflash_inject_context_kv(&c, &w, &cache, aux.data(), 4095, 16, pos, slots, dummy(0x900000), 1 << 30,
                                  nullptr) == DFLASH_ERR_INVALID_ARGUMENT);  // stride below target_hidden

@@ -112,18 +112,58 @@ def _dummy_weights(spec):
 def test_inject_checks_every_chunk_before_any_launch(n_rows):
     """A workspace too small for the call is reported as DFLASH_ERR_WORKSPACE_TOO_SMALL before
     anything is enqueued: with no GPU here, a call that reached a launch would fail with
-    DFLASH_ERR_HIP instead."""
+    DFLASH_ERR_HIP instead. The size query is the maximum over every chunk size up to its row
+    count (a 4096-row chunk on the wide fc tile needs less than some smaller chunks), so the
+    workspaces tried are ones too small for every chunk of the call: 256 bytes, and for the
+    calls with a 4096-row chunk the query's answer for 16 rows."""
     spec = synth.QWEN3_8B_DRAFTER
     cfg = binding.make_config(spec)
     w, cache, keep = _dummy_weights(spec)
     L = binding.lib()
     aux = (ctypes.c_void_p * spec.n_aux)(*[0xC0000 + 64 * j for j in range(spec.n_aux)])
-    need = binding.workspace_bytes(cfg, binding.DFLASH_OP_INJECT, n_rows)
-    for ws_bytes in (256, need // 2):
+    need16 = binding.workspace_bytes(cfg, binding.DFLASH_OP_INJECT, 16)
+    for ws_bytes in (256,) + ((need16,) if n_rows >= 4096 else ()):
         st = L.dflash_inject_context_kv(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), aux,
                                         spec.target_hidden, n_rows, 0xD0000, 0xE0000, 0xF0000, ws_bytes, None)
         assert st == -3, (n_rows, ws_bytes, st, L.dflash_last_error())
         assert b"workspace" in L.dflash_last_error()
+
+
+def test_inject_refuses_a_larger_later_chunk_before_the_first_launch():
+    """Chunks of different sizes need different workspaces, not growing with the rows (a 4096-row
+    chunk on the wide fc tile needs less than the most demanding smaller chunk, whose K split
+    keeps partials). With a workspace one byte short of that chunk's need, a 4096-row call
+    passes the check and reaches the HIP runtime (DFLASH_ERR_HIP here, with no GPU), while a
+    call of 4096 rows plus that chunk as its tail is refused before its first chunk is
+    enqueued. The 4096-row call passes validation with dummy pointers, so the test runs only
+    where no GPU is visible."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a call that passes validation would launch kernels on dummy pointers")
+    spec = synth.QWEN3_8B_DRAFTER
+    cfg = binding.make_config(spec)
+    w, cache, keep = _dummy_weights(spec)
+    L = binding.lib()
+    aux = (ctypes.c_void_p * spec.n_aux)(*[0xC0000 + 64 * j for j in range(spec.n_aux)])
+    q = lambda r: binding.workspace_bytes(cfg, binding.DFLASH_OP_INJECT, r)  # max over chunks up to r
+    top = q(4095)
+    lo, hi = 1, 4095  # the smallest chunk size that needs `top`
+    while lo < hi:
+        mid = (lo + hi) // 2
+        lo, hi = (lo, mid) if q(mid) >= top else (mid + 1, hi)
+    r = lo
+
+    def call(n_rows):
+        return L.dflash_inject_context_kv(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), aux,
+                                          spec.target_hidden, n_rows, 0xD0000, 0xE0000, 0xF0000, top - 1, None)
+    assert call(r) == -3
+    st = call(4096)
+    if st == -3:
+        pytest.skip("the 4096-row chunk needs the most workspace: no later chunk can need more")
+    assert st == -4, (st, L.dflash_last_error())  # passed the check, reached a launch
+    st = call(4096 + r)
+    assert st == -3, (r, st, L.dflash_last_error())
+    assert b"workspace" in L.dflash_last_error()
 
 
 def test_propose_checks_workspace_before_any_launch():
