@@ -530,26 +530,41 @@ __global__ __launch_bounds__(CW *KW * 64, MT > 1 ? 1 : CW * KW == 4 ? 4 : (NCG =
       if (threadIdx.x == 0) s_flag = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       if (s_flag != (unsigned)(S - 1)) continue;  // another split finishes this tile
-      for (int e = threadIdx.x; e < NACC * TR * TC; e += NT) {
+      // the loads of all this thread's elements, 8 splits each, in flight together (one round
+      // trip for up to 8 splits, not one per element); every load is issued (past the last
+      // split, or for an element outside the output, a valid address whose value is dropped),
+      // and each element is summed in split order
+      constexpr int JR = (NACC * TR * TC + NT - 1) / NT;
+      float sum[JR];
+      const float *src[JR];
+      bool keep[JR];
+#pragma unroll
+      for (int j = 0; j < JR; ++j) {
+        const int e = threadIdx.x + j * NT;
         const int a = e / (TR * TC), row = (e / TC) % TR, col = e % TC;
         const int m = m0 + row, n = n0 + col;
-        float s = 0.f;
-        if (m < g.M && n < g.N) {
-          const float *src = g.part + ((size_t)m * NACC + a) * g.N + n;
-          // loads in groups of 8 in flight, summed in split order
-          for (int q0 = 0; q0 < S; q0 += 8) {
-            float v[8];
+        keep[j] = e < NACC * TR * TC && m < g.M && n < g.N;
+        src[j] = keep[j] ? g.part + ((size_t)m * NACC + a) * g.N + n : g.part;
+        sum[j] = 0.f;
+      }
+      for (int q0 = 0; q0 < S; q0 += 8) {
+        float v[JR][8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-              v[u] = q0 + u < S ? __hip_atomic_load(src + (size_t)(q0 + u) * pstride, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT)
-                                : 0.f;
+        for (int j = 0; j < JR; ++j)
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-              if (q0 + u < S) s += v[u];
-          }
-        }
-        fin[e] = s;
+          for (int u = 0; u < 8; ++u)
+            v[j][u] = __hip_atomic_load(src[j] + (size_t)min(q0 + u, S - 1) * pstride, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < JR; ++j)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (keep[j] && q0 + u < S) sum[j] += v[j][u];
+      }
+#pragma unroll
+      for (int j = 0; j < JR; ++j) {
+        const int e = threadIdx.x + j * NT;
+        if (e < NACC * TR * TC) fin[e] = sum[j];
       }
       if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
@@ -880,31 +895,42 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
     if (s_flag != (unsigned)(splits - 1)) return;  // another split finishes this tile
     if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  for (int h = 0; h < 2; ++h) {
-    const int mh = m0 + h * HM;  // first output row of this half
-    __syncthreads();             // the previous half's epilogue is done with the LDS tile
-    if (splits > 1) {
-      for (int e = threadIdx.x; e < HM * BN; e += NT) {
-        const float *src = g.part + tbase + h * HM * BN + e;
-        float sum = 0.f;
-        for (int q0 = 0; q0 < splits; q0 += 4) {  // loads of 4 splits in flight, summed in split order
-          float v[4];
+  // the piece's sums of every split into fin (last split to arrive), or the work-group's own
+  // accumulators; then the epilogue. Two loops, so that the accumulators are dead while the
+  // reduce has its loads in flight.
+  auto reduce_to_fin = [&](int h) {
+    // 8 elements x 8 splits of loads in flight per round trip (every load issued: past the
+    // last split the address is the last split's, its value dropped), summed in split order
+    constexpr int EPT = HM * BN / NT;  // elements of the piece per thread
+    static_assert(EPT * NT == HM * BN && EPT % 8 == 0, "reduce chunks");
+    for (int j0 = 0; j0 < EPT; j0 += 8) {
+      float sum[8];
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            v[u] = q0 + u < splits ? __hip_atomic_load(src + (size_t)(q0 + u) * tstride, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT)
-                                   : 0.f;
+      for (int jj = 0; jj < 8; ++jj) sum[jj] = 0.f;
+      for (int q0 = 0; q0 < splits; q0 += 8) {
+        float v[8][8];
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (q0 + u < splits) sum += v[u];
-        }
-        fin[(e / BN) * FS + e % BN] = sum;
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            v[jj][u] = __hip_atomic_load(g.part + tbase + h * HM * BN + threadIdx.x + (j0 + jj) * NT +
+                                             (size_t)min(q0 + u, splits - 1) * tstride,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (q0 + u < splits) sum[jj] += v[jj][u];
       }
-    } else {
-      acc_to_fin(h);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int e = threadIdx.x + (j0 + jj) * NT;
+        fin[(e / BN) * FS + e % BN] = sum[jj];
+      }
     }
-    __syncthreads();
-    if (mh >= g.M) break;  // rows past M: nothing to store (uniform)
+  };
+  auto epilogue = [&](int h) {
+    const int mh = m0 + h * HM;  // first output row of this piece
     if constexpr (E == GemmEpi::kStore || E == GemmEpi::kResidAdd) {
       for (int e = threadIdx.x; e < HM * BN; e += NT) {
         const int row = e / BN, col = e % BN;
@@ -924,7 +950,7 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
         const int row = threadIdx.x / TPR, sub = threadIdx.x % TPR;
         float sq = 0.f;
         for (int c = sub; c < BN; c += TPR) sq += fin[row * FS + c];
-#pragma unroll
+  #pragma unroll
         for (int o = 1; o < TPR; o <<= 1) sq += __shfl_xor(sq, o, 64);
         if (sub == 0 && mh + row < g.M) g.ss_out[(size_t)nt * g.M + mh + row] = sq;
       }
@@ -943,7 +969,7 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
       int bi = 0x7fffffff;
       for (int c = sub; c < BN; c += TPR)
         if (n0 + c < g.N) argmax_merge(best, bi, fin[row * FS + c], n0 + c);
-#pragma unroll
+  #pragma unroll
       for (int o = 1; o < TPR; o <<= 1) {
         const float ov = __shfl_xor(best, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
@@ -964,6 +990,23 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
         head_epilogue<uint16_t, E>(g, n0 / D + hh, m, fin[row * FS + hh * D + i1],
                                    fin[row * FS + hh * D + i1 + half], own, i1, D);
       }
+    }
+  };
+  if (splits > 1) {
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();  // the previous piece's epilogue is done with the LDS tile
+      reduce_to_fin(h);
+      __syncthreads();
+      if (m0 + h * HM >= g.M) break;  // rows past M: nothing to store (uniform)
+      epilogue(h);
+    }
+  } else {
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();
+      acc_to_fin(h);
+      __syncthreads();
+      if (m0 + h * HM >= g.M) break;
+      epilogue(h);
     }
   }
 }
@@ -1143,31 +1186,42 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
     if (s_flag != (unsigned)(splits - 1)) return;  // another split finishes this tile
     if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  for (int h = 0; h < BM / HM; ++h) {
-    const int mh = m0 + h * HM;  // first output row of this piece
-    __syncthreads();             // the previous piece (or the K loop) is done with the LDS
-    if (splits > 1) {
-      for (int e = threadIdx.x; e < HM * BN; e += NT) {
-        const float *src = g.part + tbase + h * HM * BN + e;
-        float sum = 0.f;
-        for (int q0 = 0; q0 < splits; q0 += 4) {  // loads of 4 splits in flight, summed in split order
-          float v[4];
+  // the piece's sums of every split into fin (last split to arrive), or the work-group's own
+  // accumulators; then the epilogue. Two loops, so that the accumulators are dead while the
+  // reduce has its loads in flight.
+  auto reduce_to_fin = [&](int h) {
+    // 8 elements x 8 splits of loads in flight per round trip (every load issued: past the
+    // last split the address is the last split's, its value dropped), summed in split order
+    constexpr int EPT = HM * BN / NT;  // elements of the piece per thread
+    static_assert(EPT * NT == HM * BN && EPT % 8 == 0, "reduce chunks");
+    for (int j0 = 0; j0 < EPT; j0 += 8) {
+      float sum[8];
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            v[u] = q0 + u < splits ? __hip_atomic_load(src + (size_t)(q0 + u) * tstride, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT)
-                                   : 0.f;
+      for (int jj = 0; jj < 8; ++jj) sum[jj] = 0.f;
+      for (int q0 = 0; q0 < splits; q0 += 8) {
+        float v[8][8];
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (q0 + u < splits) sum += v[u];
-        }
-        fin[(e / BN) * FS + e % BN] = sum;
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            v[jj][u] = __hip_atomic_load(g.part + tbase + h * HM * BN + threadIdx.x + (j0 + jj) * NT +
+                                             (size_t)min(q0 + u, splits - 1) * tstride,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (q0 + u < splits) sum[jj] += v[jj][u];
       }
-    } else {
-      acc_to_fin(h);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int e = threadIdx.x + (j0 + jj) * NT;
+        fin[(e / BN) * FS + e % BN] = sum[jj];
+      }
     }
-    __syncthreads();
-    if (mh >= g.M) break;  // rows past M: nothing to store (uniform)
+  };
+  auto epilogue = [&](int h) {
+    const int mh = m0 + h * HM;  // first output row of this piece
     if constexpr (E == GemmEpi::kStore) {
       for (int e = threadIdx.x; e < HM * BN; e += NT) {
         const int row = e / BN, col = e % BN, m = mh + row, n = n0 + col;
@@ -1184,7 +1238,7 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
         const int row = threadIdx.x / TPR, sub = threadIdx.x % TPR;
         float sq = 0.f;
         for (int c = sub; c < BN; c += TPR) sq += fin[row * FS + c];
-#pragma unroll
+  #pragma unroll
         for (int o = 1; o < TPR; o <<= 1) sq += __shfl_xor(sq, o, 64);
         if (sub == 0 && mh + row < g.M) g.ss_out[(size_t)nt * g.M + mh + row] = sq;
       }
@@ -1202,7 +1256,7 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
       int bi = 0x7fffffff;
       for (int c = sub; c < BN; c += TPR)
         if (n0 + c < g.N) argmax_merge(best, bi, fin[row * FS + c], n0 + c);
-#pragma unroll
+  #pragma unroll
       for (int o = 1; o < TPR; o <<= 1) {
         const float ov = __shfl_xor(best, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
@@ -1212,6 +1266,23 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
         g.amax_val[(size_t)(mh + row) * ntiles + nt] = best;
         g.amax_idx[(size_t)(mh + row) * ntiles + nt] = bi;
       }
+    }
+  };
+  if (splits > 1) {
+    for (int h = 0; h < BM / HM; ++h) {
+      __syncthreads();  // the previous piece's epilogue is done with the LDS tile
+      reduce_to_fin(h);
+      __syncthreads();
+      if (m0 + h * HM >= g.M) break;  // rows past M: nothing to store (uniform)
+      epilogue(h);
+    }
+  } else {
+    for (int h = 0; h < BM / HM; ++h) {
+      __syncthreads();
+      acc_to_fin(h);
+      __syncthreads();
+      if (m0 + h * HM >= g.M) break;
+      epilogue(h);
     }
   }
 }
