@@ -1016,34 +1016,38 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
 //      K in steps of 32 with three steps in flight (register sets and LDS buffers, XOR-swizzled
 //      row-major tiles as above). A work-group loads 2.5 times fewer bytes per flop than a
 //      64 x 256 tile, which is what bounds the smaller tile: its loads at full MFMA rate would
-//      exceed what a CU's vector-memory path delivers. A is either the bf16 plane of fp32 rows
-//      (the LM head and gate|up with many rows; never K-split) or bf16 rows read in place in
-//      K segments (fc over the auxiliary target states; with fewer tiles than CUs, K is split
-//      over work-groups and the last split of a tile reduces, as in the tiled kernel). The tile
-//      then goes through LDS in four pieces of 64 rows to the SwiGLU, per-tile argmax or store
-//      (with per-tile row sums of squares) epilogue.
+//      exceed what a CU's vector-memory path delivers. A is the bf16 plane of fp32 rows (the LM
+//      head and gate|up with many rows; never K-split), bf16 rows read in place in K segments
+//      (fc over the auxiliary target states), or the (hi, lo) pair of fp32 rows (the down
+//      projection at batch 128: two MFMAs per fragment, two K steps in flight). With fewer
+//      tiles than CUs, K is split over work-groups and the last split of a tile reduces, as in
+//      the tiled kernel. The tile then goes through LDS in four pieces of 64 rows to the SwiGLU,
+//      per-tile argmax, or store / residual add (with per-tile row sums of squares) epilogue.
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kWideM = 256, kWideN = 256, kWideWaves = 8, kWidePiece = 64;
 constexpr int kWideStages = 3;
 constexpr size_t kWideLds = (size_t)kWideStages * (kWideM + kWideN) * kTileK * 2;
+constexpr size_t kWideLdsPair = (size_t)2 * (2 * kWideM + kWideN) * kTileK * 2;
 
-template <GemmEpi E, bool kSeg>
+template <GemmEpi E, bool kSeg, bool kLo>
 __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs g, int mtiles, int ntiles, int nsplit) {
-  static_assert(kSeg ? E == GemmEpi::kStore : (E == GemmEpi::kSwiGLU || E == GemmEpi::kArgmax), "wide tile epilogues");
-  constexpr int BM = kWideM, BN = kWideN, BK = kTileK, NS = kWideStages, HM = kWidePiece;
+  static_assert(kSeg ? E == GemmEpi::kStore
+                     : kLo ? E == GemmEpi::kResidAdd : (E == GemmEpi::kSwiGLU || E == GemmEpi::kArgmax),
+                "wide tile epilogues");
+  constexpr int BM = kWideM, BN = kWideN, BK = kTileK, NS = kLo ? 2 : kWideStages, HM = kWidePiece;
   constexpr int NT = kWideWaves * 64, NW = kWideWaves, WR = 4, WC = 2;
   constexpr int WM = BM / WR, WN = BN / WC, TF = WM / 32, UN = WN / 32;  // 32 x 32 MFMA tiles per wave
   constexpr int JA = BM * 4 / NT, JW = BN * 4 / NT;                  // 16-byte loads per thread, plane and step
-  constexpr int NLD = JA + JW;
+  constexpr int NLD = (kLo ? 2 : 1) * JA + JW;
   static_assert(JA * NT == BM * 4 && JW * NT == BN * 4 && HM == WM, "one epilogue piece per wave row");
-  constexpr size_t kAB = (size_t)BM * BK * 2, kWB = (size_t)BN * BK * 2;
+  constexpr size_t kPlane = (size_t)BM * BK * 2, kAB = (kLo ? 2 : 1) * kPlane, kWB = (size_t)BN * BK * 2;
   static_assert((size_t)HM * (BN + 4) * 4 <= kWideLds, "epilogue piece fits the K-loop buffers");
   constexpr bool kDual = E == GemmEpi::kSwiGLU;
   constexpr int OC = kDual ? BN / 2 : BN;  // output columns of a tile (SwiGLU: BN/2 gate + BN/2 up rows)
   constexpr int FS = BN + 4, TPR = NT / HM;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ unsigned s_flag;
-  const int splits = kSeg ? nsplit : 1;  // the bf16-plane tiles are never split
+  const int splits = kSeg || kLo ? nsplit : 1;  // the bf16-plane tiles are never split
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WC, wn = wave % WC;
   // work-group -> (column tile, row tile, K split): the row tiles and splits of a column tile run
   // back to back on one XCD (ids congruent mod 8), sharing the weight tile through its L2
@@ -1069,7 +1073,8 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
               ((lane & 3) ^ ((r >> 2) & 3)) * 8;
   }
   const uint16_t *ahi = reinterpret_cast<const uint16_t *>(g.a[0]);
-  Vec16 areg[NS][JA], wreg[NS][JW];
+  const uint16_t *alo = reinterpret_cast<const uint16_t *>(g.a[kLo ? 1 : 0]);
+  Vec16 areg[NS][JA], lreg[NS][kLo ? JA : 1], wreg[NS][JW];
   const int kseg = K / g.a_nseg;  // bf16 A in segments: K columns per segment
   auto load = [&](int set, int k0) {
     if constexpr (kSeg) {  // the segment of the concatenated A holding columns [k0, k0 + BK)
@@ -1079,7 +1084,10 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
       for (int j = 0; j < JA; ++j) areg[set][j] = load_vec16(a0 + aoff[j]);
     } else {
 #pragma unroll
-      for (int j = 0; j < JA; ++j) areg[set][j] = load_vec16(ahi + aoff[j] + k0);
+      for (int j = 0; j < JA; ++j) {
+        areg[set][j] = load_vec16(ahi + aoff[j] + k0);
+        if constexpr (kLo) lreg[set][j] = load_vec16(alo + aoff[j] + k0);
+      }
     }
 #pragma unroll
     for (int j = 0; j < JW; ++j) wreg[set][j] = load_vec16(brow[j] + k0);
@@ -1087,7 +1095,10 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
   auto store = [&](int set) {
     unsigned char *sa = smem + set * kAB, *sw = smem + NS * kAB + set * kWB;
 #pragma unroll
-    for (int j = 0; j < JA; ++j) *reinterpret_cast<uint4 *>(sa + (j * NW + wave) * 1024 + lane * 16) = areg[set][j].u;
+    for (int j = 0; j < JA; ++j) {
+      *reinterpret_cast<uint4 *>(sa + (j * NW + wave) * 1024 + lane * 16) = areg[set][j].u;
+      if constexpr (kLo) *reinterpret_cast<uint4 *>(sa + kPlane + (j * NW + wave) * 1024 + lane * 16) = lreg[set][j].u;
+    }
 #pragma unroll
     for (int j = 0; j < JW; ++j) *reinterpret_cast<uint4 *>(sw + (j * NW + wave) * 1024 + lane * 16) = wreg[set][j].u;
   };
@@ -1121,15 +1132,19 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
       for (int u = 0; u < UN; ++u) bf[u].u = *reinterpret_cast<const uint4 *>(sw + tile_swz(wn * WN + u * 32 + (lane & 31), ch));
 #pragma unroll
       for (int t = 0; t < TF; ++t) {
-        Vec16 ah;
-        ah.u = *reinterpret_cast<const uint4 *>(sa + tile_swz(wm * WM + t * 32 + (lane & 31), ch));
-        bf16x8_t av;
+        const int o = tile_swz(wm * WM + t * 32 + (lane & 31), ch);
+        Vec16 ah, al;
+        ah.u = *reinterpret_cast<const uint4 *>(sa + o);
+        if constexpr (kLo) al.u = *reinterpret_cast<const uint4 *>(sa + kPlane + o);
+        bf16x8_t av, lv;
         __builtin_memcpy(&av, &ah.u, 16);
+        if constexpr (kLo) __builtin_memcpy(&lv, &al.u, 16);
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
           bf16x8_t bv;
           __builtin_memcpy(&bv, &bf[u].u, 16);
           acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[t][u], 0, 0, 0);
+          if constexpr (kLo) acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lv, bv, acc[t][u], 0, 0, 0);
         }
       }
     }
@@ -1137,15 +1152,14 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
     if (ks + 1 < nk) store(nxt);
     __syncthreads();
   };
-  static_assert(NS == 3, "the loop below is unrolled by three");
   int ks = 0;
-  for (; ks + 2 < nk; ks += 3) {
+  for (; ks + NS - 1 < nk; ks += NS) {  // unrolled by NS (two or three)
     step(std::integral_constant<int, 0>{}, ks);
     step(std::integral_constant<int, 1>{}, ks + 1);
-    step(std::integral_constant<int, 2>{}, ks + 2);
+    if constexpr (NS > 2) step(std::integral_constant<int, 2 % NS>{}, ks + 2);
   }
   if (ks < nk) step(std::integral_constant<int, 0>{}, ks);
-  if (ks + 1 < nk) step(std::integral_constant<int, 1>{}, ks + 1);
+  if (NS > 2 && ks + 1 < nk) step(std::integral_constant<int, 1>{}, ks + 1);
   __builtin_amdgcn_s_waitcnt(0);  // the clamped loads past the end
 
   // ---- the tile through LDS, one piece of 64 rows at a time: piece h is held by the waves
@@ -1222,12 +1236,14 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
   };
   auto epilogue = [&](int h) {
     const int mh = m0 + h * HM;  // first output row of this piece
-    if constexpr (E == GemmEpi::kStore) {
+    if constexpr (E == GemmEpi::kStore || E == GemmEpi::kResidAdd) {
       for (int e = threadIdx.x; e < HM * BN; e += NT) {
         const int row = e / BN, col = e % BN, m = mh + row, n = n0 + col;
         float v = fin[row * FS + col];
         if (m < g.M && n < g.N) {
-          g.out[(size_t)m * g.N + n] = v;
+          const size_t o = (size_t)m * g.N + n;
+          if (E == GemmEpi::kResidAdd) v += g.out[o];
+          g.out[o] = v;
         } else {
           v = 0.f;
         }
@@ -1289,12 +1305,30 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
 
 // bf16 A in segments (fc over the auxiliary target states), read in place
 hipError_t launch_wide_seg(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
-  auto kern = gemm_wide_kernel<GemmEpi::kStore, true>;
+  auto kern = gemm_wide_kernel<GemmEpi::kStore, true, false>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds);
   if (attr != hipSuccess) return attr;
   const int ntiles = p.col_groups, mtiles = p.row_blocks;
   kern<<<(ntiles + 7) / 8 * 8 * mtiles * p.splits, kWideWaves * 64, kWideLds, s>>>(g, mtiles, ntiles, p.splits);
+  return hipGetLastError();
+}
+
+// the fp32 rows as their (hi, lo) pair, then the wide-tile kernel with the residual add
+hipError_t launch_wide_pair(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
+  auto kern = gemm_wide_kernel<GemmEpi::kResidAdd, false, true>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLdsPair);
+  if (attr != hipSuccess) return attr;
+  uint16_t *hi = g.a_split, *lo = g.a_split + (size_t)g.M * g.K;
+  split_rows_kernel<<<g.M, 256, 0, s>>>(g, hi, lo);
+  GemmArgs t = g;
+  t.a[0] = hi;
+  t.a[1] = lo;
+  t.a_nseg = 1;
+  t.lda = g.K;
+  const int ntiles = p.col_groups, mtiles = p.row_blocks;
+  kern<<<(ntiles + 7) / 8 * 8 * mtiles * p.splits, kWideWaves * 64, kWideLdsPair, s>>>(t, mtiles, ntiles, p.splits);
   return hipGetLastError();
 }
 
@@ -1304,7 +1338,7 @@ hipError_t launch_wide(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
   if constexpr (E != GemmEpi::kSwiGLU && E != GemmEpi::kArgmax) {
     return hipErrorInvalidValue;
   } else {
-    auto kern = gemm_wide_kernel<E, false>;
+    auto kern = gemm_wide_kernel<E, false, false>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds);
     if (attr != hipSuccess) return attr;
@@ -1354,9 +1388,11 @@ hipError_t launch_tiled_shape(const GemmArgs &g, const GemmPlan &p, hipStream_t 
 
 template <GemmEpi E, bool kLo>
 hipError_t launch_tiled(const GemmArgs &g, const GemmPlan &p, hipStream_t s) {
-  if (p.tile_m == kWideM) {  // the bf16 plane of fp32 rows (SwiGLU, argmax), or fc's bf16 segments
+  if (p.tile_m == kWideM) {  // bf16 plane (SwiGLU, argmax), fc's bf16 segments, or the pair (residual add)
     if constexpr (E == GemmEpi::kStore && !kLo)
       return launch_wide_seg(g, p, s);
+    else if constexpr (E == GemmEpi::kResidAdd)
+      return launch_wide_pair(g, p, s);
     else
       return launch_wide<E>(g, p, s);
   }
@@ -1525,6 +1561,21 @@ GemmPlan gemm_plan(int M, int N, int K, int head_dim, bool bf16, GemmEpi epi, bo
         if (cost < best - 1e-9) best = cost, p.splits = s;
       }
     }
+    // The down projection (residual add, K >= 2 N) of at least four wide row tiles takes the wide
+    // tile on the (hi, lo) pair, K split toward one round (batch 128: 2.11 -> 1.89 ms per step);
+    // with fewer rows, and for O, the 64 x 256 tiles measured faster.
+    if (!p.hi_only && a_f32 && epi == GemmEpi::kResidAdd && wide && K >= 2 * N && M > 3 * kWideM) {
+      p.tile_m = kWideM;
+      p.tile_n = kWideN;
+      p.col_groups = (N + p.tile_n - 1) / p.tile_n;
+      p.row_blocks = (M + p.tile_m - 1) / p.tile_m;
+      const long tiles = (long)p.col_groups * p.row_blocks;
+      double best = 1e30;
+      for (int s = smin; s <= 8 && 16 * s <= K / kTileK; ++s) {
+        const double cost = (double)((tiles * s + slots - 1) / slots) / s + 0.03 * (s - 1);
+        if (cost < best - 1e-9) best = cost, p.splits = s;
+      }
+    }
     // fc (bf16 rows in K segments, more than one wide row tile) takes the wide tile too, K split
     // toward one round of work-groups (at least 64 K steps a split): batch 128 0.41 -> 0.29 ms,
     // batch 32 0.47 -> 0.40 ms per step
@@ -1600,7 +1651,8 @@ hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, const GemmPla
         (p.tile_m == 64 && p.tile_n == 256) ||
         (p.tile_m == kWideM && p.tile_n == kWideN && p.hi_only && p.splits == 1 && g0.a_f32 &&
          (epi == GemmEpi::kSwiGLU || (epi == GemmEpi::kArgmax && g0.b_nseg == 1))) ||
-        (p.tile_m == kWideM && p.tile_n == kWideN && !g0.a_f32 && epi == GemmEpi::kStore && g0.b_nseg == 1)) || g0.b_nseg < 1 || g0.b_nseg > 3 || p.splits < 1 ||
+        (p.tile_m == kWideM && p.tile_n == kWideN && !g0.a_f32 && epi == GemmEpi::kStore && g0.b_nseg == 1) ||
+        (p.tile_m == kWideM && p.tile_n == kWideN && g0.a_f32 && !p.hi_only && epi == GemmEpi::kResidAdd && g0.b_nseg == 1)) || g0.b_nseg < 1 || g0.b_nseg > 3 || p.splits < 1 ||
         p.splits > g0.K / kTileK || (p.splits > 1 && (!g0.part || !g0.counters)) ||
         (head && ((g0.head_dim != 64 && g0.head_dim != 128) || g0.N % g0.head_dim)))
       return hipErrorInvalidValue;
