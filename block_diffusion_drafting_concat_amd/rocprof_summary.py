@@ -49,9 +49,10 @@ def short_name(name: str) -> str:
     if m:
         return (f"gemm_tiled_kernel<{EPI[m.group(1)]},{'hi+lo-A' if m.group(2) == 'true' else 'bf16-A'},"
                 f"{m.group(3)}x{m.group(4)}>")
-    m = re.search(r"gemm_wide_kernel<\(dflash::GemmEpi\)(\d), (true|false)>", name)
+    m = re.search(r"gemm_wide_kernel<\(dflash::GemmEpi\)(\d), (true|false), (true|false)>", name)
     if m:
-        return f"gemm_wide_kernel<{EPI[m.group(1)]},{'bf16-A-segments' if m.group(2) == 'true' else 'bf16-A'},256x256>"
+        a_kind = "bf16-A-segments" if m.group(2) == "true" else "hi+lo-A" if m.group(3) == "true" else "bf16-A"
+        return f"gemm_wide_kernel<{EPI[m.group(1)]},{a_kind},256x256>"
     if name.startswith("Cijk_"):  # a library GEMM kernel (bench.py's attainable-rate check)
         return "library bf16 GEMM (" + name.split("_MT")[1].split("_")[0] + " tiles)" if "_MT" in name else name[:40]
     name = re.sub(r"^void ", "", name)
