@@ -100,7 +100,7 @@ struct GemmPlan {
   int col_groups, row_blocks;  // output tiles = col_groups * row_blocks (split-K counters)
   int tiled;                   // 1: the LDS-tiled kernel for many rows (tile_m x tile_n output tiles)
   int hi_only;                 // tiled, fp32 activations: only their bf16 rounding enters the MFMAs
-  int tile_m, tile_n;          // tiled: 128 x 128, 64 x 256, or the wide 256 x 256 (bf16 plane alone)
+  int tile_m, tile_n;          // tiled: 128 x 128, 64 x 256, or the wide 256 x 256 (gemm_wide_kernel)
 };
 // a_f32: the activations are fp32 rows (else the storage type, as the auxiliary target states,
 // in a_segs equal K segments)
