@@ -601,10 +601,15 @@ dflash_status propose_enqueue(const dflash_config *cfg, const dflash_weights *w,
     gu.b_end[1] = I;
     gu.b_nseg = 2;
     gu.out = act;
+    // many rows: gate|up writes its product as the (hi, lo) planes the down projection takes,
+    // in the act buffer (two bf16 planes fill its M x I floats), so no split pass runs
+    const bool act_planes = p.gu.tiled && p.down.tiled && !p.down.hi_only;
+    if (act_planes) gu.out_planes = reinterpret_cast<uint16_t *>(act);
     HIP_TRY(launch_gemm(gu, bf, GemmEpi::kSwiGLU, p.gu, s));
 
     GemmArgs gd = gemm_args(cfg, "gemm.down", act, I, M, H, I, ctr, part);
     gd.a_split = asplit;
+    if (act_planes) gd.a_planes = reinterpret_cast<const uint16_t *>(act);
     gd.b[0] = w->w_down[l];
     gd.b_end[0] = H;
     gd.out = x;

@@ -674,6 +674,35 @@ template <int BM, int BN> struct TileLds {
   }
 };
 
+// a SwiGLU output element o = m * N + n: fp32, or its (hi, lo) bf16 planes for a consumer that
+// takes the pair (the down projection with many rows), exactly as split_rows_kernel splits
+__device__ __forceinline__ void store_swiglu(const GemmArgs &g, size_t o, float v) {
+  if (g.out_planes) {
+    const uint16_t h = f32_to_bf16(v);
+    g.out_planes[o] = h;
+    g.out_planes[(size_t)g.M * g.N + o] = f32_to_bf16(v - bf16_to_f32(h));
+  } else {
+    g.out[o] = v;
+  }
+}
+
+// two adjacent SwiGLU output elements o, o + 1 (o even, N even: 4- or 8-byte aligned) in one
+// store per plane; the pairs convert with v_cvt_pk_bf16_f32, whose round to nearest even gives
+// the same bits as f32_to_bf16 (NaN aside)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_swiglu2(const GemmArgs &g, size_t o, float v0, float v1) {
+  if (g.out_planes) {
+    const bf16x2_t h = __builtin_convertvector(f32x2_t{v0, v1}, bf16x2_t);
+    const float h0 = (float)h[0], h1 = (float)h[1];
+    const bf16x2_t l = __builtin_convertvector(f32x2_t{v0 - h0, v1 - h1}, bf16x2_t);
+    __builtin_memcpy(g.out_planes + o, &h, 4);
+    __builtin_memcpy(g.out_planes + (size_t)g.M * g.N + o, &l, 4);
+  } else {
+    *reinterpret_cast<float2 *>(g.out + o) = make_float2(v0, v1);
+  }
+}
+
 __device__ __forceinline__ int tile_swz(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
 
 // The activations of the tiled GEMM, once per launch: row m of A (the kept rows of the block
@@ -955,12 +984,23 @@ __global__ __launch_bounds__(256, 3) void gemm_tiled_kernel(GemmArgs g, int mtil
         if (sub == 0 && mh + row < g.M) g.ss_out[(size_t)nt * g.M + mh + row] = sq;
       }
     } else if constexpr (E == GemmEpi::kSwiGLU) {
-      for (int e = threadIdx.x; e < HM * OC; e += NT) {
+      static_assert(OC % 2 == 0, "column pairs");
+      for (int e = threadIdx.x * 2; e < HM * OC; e += NT * 2) {  // two adjacent columns a thread
         const int row = e / OC, col = e % OC;
         const int m = mh + row, n = n0 + col;
         if (m < g.M && n < g.N) {
-          const float gt = fin[row * FS + col], up = fin[row * FS + OC + col];
-          g.out[(size_t)m * g.N + n] = gt / (1.f + expf(-gt)) * up;
+          const float g0 = fin[row * FS + col], u0 = fin[row * FS + OC + col];
+          const float v0 = g0 / (1.f + expf(-g0)) * u0;
+          if (n + 1 < g.N && (g.N & 1) == 0) {
+            const float g1 = fin[row * FS + col + 1], u1 = fin[row * FS + OC + col + 1];
+            store_swiglu2(g, (size_t)m * g.N + n, v0, g1 / (1.f + expf(-g1)) * u1);
+          } else {
+            store_swiglu(g, (size_t)m * g.N + n, v0);
+            if (n + 1 < g.N) {
+              const float g1 = fin[row * FS + col + 1], u1 = fin[row * FS + OC + col + 1];
+              store_swiglu(g, (size_t)m * g.N + n + 1, g1 / (1.f + expf(-g1)) * u1);
+            }
+          }
         }
       }
     } else if constexpr (E == GemmEpi::kArgmax) {
@@ -1259,11 +1299,21 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void gemm_wide_kernel(GemmArgs 
         if (sub == 0 && mh + row < g.M) g.ss_out[(size_t)nt * g.M + mh + row] = sq;
       }
     } else if constexpr (E == GemmEpi::kSwiGLU) {
-      for (int e = threadIdx.x; e < HM * OC; e += NT) {
+      for (int e = threadIdx.x * 2; e < HM * OC; e += NT * 2) {  // two adjacent columns a thread
         const int row = e / OC, col = e % OC, m = mh + row, n = n0 + col;
         if (m < g.M && n < g.N) {
-          const float gt = fin[row * FS + col], up = fin[row * FS + OC + col];
-          g.out[(size_t)m * g.N + n] = gt / (1.f + expf(-gt)) * up;
+          const float g0 = fin[row * FS + col], u0 = fin[row * FS + OC + col];
+          const float v0 = g0 / (1.f + expf(-g0)) * u0;
+          if (n + 1 < g.N && (g.N & 1) == 0) {
+            const float g1 = fin[row * FS + col + 1], u1 = fin[row * FS + OC + col + 1];
+            store_swiglu2(g, (size_t)m * g.N + n, v0, g1 / (1.f + expf(-g1)) * u1);
+          } else {
+            store_swiglu(g, (size_t)m * g.N + n, v0);
+            if (n + 1 < g.N) {
+              const float g1 = fin[row * FS + col + 1], u1 = fin[row * FS + OC + col + 1];
+              store_swiglu(g, (size_t)m * g.N + n + 1, g1 / (1.f + expf(-g1)) * u1);
+            }
+          }
         }
       }
     } else {
@@ -1320,8 +1370,13 @@ hipError_t launch_wide_pair(const GemmArgs &g, const GemmPlan &p, hipStream_t s)
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLdsPair);
   if (attr != hipSuccess) return attr;
-  uint16_t *hi = g.a_split, *lo = g.a_split + (size_t)g.M * g.K;
-  split_rows_kernel<<<g.M, 256, 0, s>>>(g, hi, lo);
+  const uint16_t *hi = g.a_split, *lo = g.a_split + (size_t)g.M * g.K;
+  if (g.a_planes) {  // split by the producer
+    hi = g.a_planes;
+    lo = g.a_planes + (size_t)g.M * g.K;
+  } else {
+    split_rows_kernel<<<g.M, 256, 0, s>>>(g, g.a_split, g.a_split + (size_t)g.M * g.K);
+  }
   GemmArgs t = g;
   t.a[0] = hi;
   t.a[1] = lo;
@@ -1364,8 +1419,13 @@ hipError_t launch_tiled_shape(const GemmArgs &g, const GemmPlan &p, hipStream_t 
   const int ntiles = p.col_groups, mtiles = p.row_blocks;
   GemmArgs t = g;
   if constexpr (kLo) {
-    uint16_t *hi = g.a_split, *lo = g.a_split + (size_t)g.M * g.K;
-    split_rows_kernel<<<g.M, 256, 0, s>>>(g, hi, p.hi_only ? nullptr : lo);
+    const uint16_t *hi = g.a_split, *lo = g.a_split + (size_t)g.M * g.K;
+    if (g.a_planes && !p.hi_only) {  // split by the producer
+      hi = g.a_planes;
+      lo = g.a_planes + (size_t)g.M * g.K;
+    } else {
+      split_rows_kernel<<<g.M, 256, 0, s>>>(g, g.a_split, p.hi_only ? nullptr : g.a_split + (size_t)g.M * g.K);
+    }
     t.a[0] = hi;
     t.a[1] = lo;
     t.a_nseg = 1;
@@ -1646,7 +1706,12 @@ hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, const GemmPla
                                : epi == GemmEpi::kStore && g0.a_nseg >= 1 && g0.a_nseg <= 8 &&
                                      g0.K % g0.a_nseg == 0 && (g0.K / g0.a_nseg) % kTileK == 0 && !g0.norm_w &&
                                      !g0.a_out && g0.keep_bs == 0 && g0.lda % 8 == 0;
-    if (!bf16 || !a_ok || g0.K % kTileK || g0.M < 1 || g0.keep_bs == 1 || p.col_groups != (g0.N + oc - 1) / oc ||
+    // planes written by the producer: the pair of rows with no norm on load or compaction; planes
+    // as output: SwiGLU only
+    const bool planes_ok = (!g0.a_planes || (g0.a_f32 && !p.hi_only && !g0.norm_w && !g0.a_out && !g0.keep_bs)) &&
+                           (!g0.out_planes || epi == GemmEpi::kSwiGLU);
+    if (!bf16 || !a_ok || !planes_ok || g0.K % kTileK || g0.M < 1 || g0.keep_bs == 1 ||
+        p.col_groups != (g0.N + oc - 1) / oc ||
         p.row_blocks != (g0.M + p.tile_m - 1) / p.tile_m || !((p.tile_m == 128 && p.tile_n == 128) ||
         (p.tile_m == 64 && p.tile_n == 256) ||
         (p.tile_m == kWideM && p.tile_n == kWideN && p.hi_only && p.splits == 1 && g0.a_f32 &&
@@ -1674,7 +1739,8 @@ hipError_t launch_gemm(const GemmArgs &g0, bool bf16, GemmEpi epi, const GemmPla
       (g0.K / splits) % step || (g0.a_nseg > 1 && (g0.K / g0.a_nseg) % (bf16 ? 8 : 4)) ||
       (splits > 1 && (!g0.part || !g0.counters)) || (head && (g0.head_dim != 64 && g0.head_dim != 128)) ||
       (head && p.cw * p.ct * 16 != g0.head_dim) || ((g0.norm_w || g0.a_out) && (g0.a_nseg > 1 || (bf16 && !g0.a_f32) || !g0.ss)) ||
-      (g0.keep_bs == 1) || p.col_groups != (g0.N + 16 * p.cw * p.ct - 1) / (16 * p.cw * p.ct))
+      (g0.keep_bs == 1) || p.col_groups != (g0.N + 16 * p.cw * p.ct - 1) / (16 * p.cw * p.ct) ||
+      g0.a_planes || g0.out_planes)  // (the streaming kernel takes and writes fp32 rows only)
     return hipErrorInvalidValue;
   GemmArgs g = g0;
   g.kt = g.K / splits;

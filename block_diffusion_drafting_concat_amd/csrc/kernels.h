@@ -84,6 +84,12 @@ struct GemmArgs {
   const char *tag;  // name under which the launch is timed when profiling is on
   int kt, kp;       // set by launch_gemm: K per split, K per staged LDS pass
   uint16_t *a_split;  // tiled plans: workspace for the (hi, lo) bf16 planes of A, 2 * M * K
+  // tiled SwiGLU: write the output as its (hi, lo) bf16 planes [2][M][N] (hi = bf16(f),
+  // lo = bf16(f - hi)) instead of fp32 rows
+  uint16_t *out_planes;
+  // tiled (hi, lo) plans: A's planes [2][M][K] as written by its producer (no split pass; A
+  // has no norm on load)
+  const uint16_t *a_planes;
 };
 
 int gemm_mt(int M);
