@@ -25,13 +25,16 @@
 //  * the KW sub-slice tiles are summed through LDS in a fixed order into the work-group's
 //    tile. With several K splits every split writes its tile to the workspace with
 //    device-scope stores and the last work-group of the output tile to arrive (a device-scope
-//    counter) sums all splits in split order. There are no float atomics, so results are
-//    deterministic;
+//    counter) sums all splits in split order, with the loads of all its elements in flight
+//    together. There are no float atomics, so results are deterministic;
 //  * the epilogue runs on the final tile: fp32 store, residual add, SwiGLU, the LM head's
 //    per-group (max, lowest index), per-head q/k RMSNorm + RoPE of the block, or the
 //    context K/V epilogue of injection (k_norm + RoPE + paged scatter). The last three
 //    need a column group to be exactly one head.
-// Up to 64 activation rows are held as MT accumulator tiles; more rows use grid.z blocks.
+// Up to 64 activation rows are held as MT accumulator tiles (more rows would use grid.z
+// blocks). gemm_plan sends more than 64 rows of a bf16 drafter to the LDS-tiled kernels further
+// down: gemm_tiled_kernel (64 x 256 or 128 x 128 tiles) and gemm_wide_kernel (256 x 256 tiles,
+// one work-group per CU).
 #include <type_traits>
 
 #include "common.h"
