@@ -572,6 +572,10 @@ dflash_status propose_enqueue(const dflash_config *cfg, const dflash_weights *w,
     at_.pm = at<float>(workspace, p.off_pm);
     at_.pl = at<float>(workspace, p.off_pl);
     at_.o = o;
+    // many rows: the merged output as the (hi, lo) planes the O projection takes, in the o
+    // buffer (two bf16 planes fill its M x QH*D floats), so O runs no split pass
+    const bool o_planes = p.o.tiled && !p.o.hi_only;
+    at_.o_planes = o_planes ? reinterpret_cast<uint16_t *>(o) : nullptr;
     HIP_TRY(wait_cache());
     if (batch > 1) {
       // the work-groups that have keys, listed once for every layer (same sequence lengths)
@@ -584,6 +588,7 @@ dflash_status propose_enqueue(const dflash_config *cfg, const dflash_weights *w,
     // O projection + residual add; the row sums of squares feed the post-attention norm
     GemmArgs go = gemm_args(cfg, "gemm.o", o, QH * D, M, H, QH * D, ctr, part);
     go.a_split = asplit;
+    if (o_planes) go.a_planes = reinterpret_cast<const uint16_t *>(o);
     go.b[0] = w->wo[l];
     go.b_end[0] = H;
     go.out = x;

@@ -28,6 +28,17 @@ namespace {
 constexpr int kTileKeys = 64;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// element e of the merged output: fp32, or its (hi, lo) bf16 planes
+__device__ __forceinline__ void store_out(const AttnArgs &a, size_t e, float v) {
+  if (a.o_planes) {
+    const uint16_t h = f32_to_bf16(v);
+    a.o_planes[e] = h;
+    a.o_planes[(size_t)a.B * a.bs * a.QH * a.D + e] = f32_to_bf16(v - bf16_to_f32(h));
+  } else {
+    a.o[e] = v;
+  }
+}
 constexpr int kMaxChunk = 16 * kTileKeys;  // keys per split at most (attn_plan)
 
 template <typename T, int D>
@@ -262,16 +273,35 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
     l_run += __shfl_xor(l_run, 32, 64);
   }
   const int G2 = a.QH / a.KVH;
-  auto out_row = [&](int row) {  // merged output row of query row `row` = hh*bs + j
-    return a.o + ((size_t)(b * a.bs + row % a.bs) * a.QH + g * G2 + row / a.bs) * D;
+  auto out_row = [&](int row) {  // merged output element index of query row `row` = hh*bs + j
+    return ((size_t)(b * a.bs + row % a.bs) * a.QH + g * G2 + row / a.bs) * D;
   };
   const int ns = (T_total + a.chunk - 1) / a.chunk;  // splits of this sequence
   if (ns == 1) {  // the whole key range: normalise in place
     if (rvalid) {
       const float inv = 1.f / l_run;
-      float *op = out_row(r) + (lane >> 4) * 4;
+      const size_t e0 = out_row(r) + (lane >> 4) * 4;
+      if (a.o_planes) {  // 4 consecutive d: packed conversions (round to nearest even), 8-byte stores
+        const size_t lo_off = (size_t)a.B * a.bs * a.QH * D;
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4_t *>(op + db * 16) = acc_o[db] * inv;
+        for (int db = 0; db < D / 16; ++db) {
+          const f32x4_t v = acc_o[db] * inv;
+          const bf16x2_t h01 = __builtin_convertvector(f32x2_t{v[0], v[1]}, bf16x2_t);
+          const bf16x2_t h23 = __builtin_convertvector(f32x2_t{v[2], v[3]}, bf16x2_t);
+          const bf16x2_t l01 = __builtin_convertvector(f32x2_t{v[0] - (float)h01[0], v[1] - (float)h01[1]}, bf16x2_t);
+          const bf16x2_t l23 = __builtin_convertvector(f32x2_t{v[2] - (float)h23[0], v[3] - (float)h23[1]}, bf16x2_t);
+          uint32_t hw[2], lw[2];
+          __builtin_memcpy(&hw[0], &h01, 4);
+          __builtin_memcpy(&hw[1], &h23, 4);
+          __builtin_memcpy(&lw[0], &l01, 4);
+          __builtin_memcpy(&lw[1], &l23, 4);
+          *reinterpret_cast<uint2 *>(a.o_planes + e0 + db * 16) = make_uint2(hw[0], hw[1]);
+          *reinterpret_cast<uint2 *>(a.o_planes + lo_off + e0 + db * 16) = make_uint2(lw[0], lw[1]);
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4_t *>(a.o + e0 + db * 16) = acc_o[db] * inv;
+      }
     }
     return;
   }
@@ -343,7 +373,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   while ((s0 += 16) < ns);
   if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel
   const int hh = row / a.bs, j = row % a.bs;
-  a.o[((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d] = o / l;
+  store_out(a, ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d, o / l);
 }
 
 // Merge of many splits (more than 16 per sequence: one long context): work-group = one
@@ -383,7 +413,7 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(AttnArgs a) {
       dn += w * sl[q];
     }
     const int hh = row / a.bs, j = row % a.bs;
-    a.o[((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d] = n / dn;
+    store_out(a, ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d, n / dn);
   }
 }
 

@@ -159,6 +159,9 @@ struct AttnArgs {
   int chunk, nsplit;    // keys per split (multiple of 64), splits per sequence
   float *po, *pm, *pl;  // partials [B][KVH][nsplit][64][D], [B][KVH][nsplit][64]
   float *o;             // merged output [M][QH*D], fp32
+  // non-null: the merged output as its (hi, lo) bf16 planes [2][M][QH*D] instead (hi =
+  // bf16(f), lo = bf16(f - hi)), for an O projection that takes the pair without a split pass
+  uint16_t *o_planes;
   // With several sequences: the (sequence, kv head, split) work-groups that have keys, as
   // flat indices (b * KVH + g) * nsplit + split, and their count (written by
   // launch_attention_items once per proposal); null: every index of the grid is launched.
