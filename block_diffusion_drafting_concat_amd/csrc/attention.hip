@@ -352,28 +352,77 @@ __device__ __forceinline__ void merge16(const float *pm, const float *pl, const 
   m_acc = m_new;
 }
 
-// Merge of up to 16 splits per sequence: thread (query row, d) of a (sequence, kv head),
-// 256 / D rows per work-group, one round trip for all splits.
+// merge16 for four consecutive output elements of one row (one 16-byte load per split): the
+// same operations, in the same order, for each of the four
+__device__ __forceinline__ void merge16x4(const float *pm, const float *pl, const float *po, size_t stride_ml,
+                                          size_t stride_o, int s0, int ns, int nmax, float &m_acc, float &l_acc,
+                                          f32x4_t &o_acc) {
+  float mv[16], lv[16];
+  f32x4_t pv[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int q = min(s0 + u, nmax - 1);
+    mv[u] = pm[(size_t)q * stride_ml];
+    lv[u] = pl[(size_t)q * stride_ml];
+    pv[u] = *reinterpret_cast<const f32x4_t *>(po + (size_t)q * stride_o);
+  }
+  float m_new = m_acc;
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (s0 + u < ns) m_new = fmaxf(m_new, mv[u]);
+  const float r = exp2f(m_acc - m_new);
+  l_acc *= r;
+  o_acc *= r;
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (s0 + u < ns) {
+      const float w = exp2f(mv[u] - m_new);
+      l_acc += w * lv[u];
+      o_acc += w * pv[u];
+    }
+  m_acc = m_new;
+}
+
+// Merge of up to 16 splits per sequence: thread (query row, 4 consecutive d) of a (sequence,
+// kv head), 1024 / D rows per work-group, one round trip for all splits (16-byte partial loads,
+// 16-byte fp32 or 8 + 8-byte plane stores).
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  const int D = a.D, rpw = 256 / D;
-  const int row = blockIdx.x * rpw + (int)threadIdx.x / D, d = threadIdx.x % D;
+  const int D = a.D, tpr = D / 4, rpw = 256 / tpr;
+  const int row = blockIdx.x * rpw + (int)threadIdx.x / tpr, d = ((int)threadIdx.x % tpr) * 4;
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = a.QH / a.KVH;
   if (row >= a.bs * G) return;
   const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
   const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64 + row;
-  float m = -INFINITY, l = 0.f, o = 0.f;
+  float m = -INFINITY, l = 0.f;
+  f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // One sequence: the first 16 splits' loads go out with the length's (clamped to the
   // workspace's splits). Several: only the sequence's own splits are read.
   const int nmax = a.B == 1 ? a.nsplit : ns;
   int s0 = 0;
-  do merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, 1, ns, nmax, m, l, o);
+  do merge16x4(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, ns, nmax, m, l, o);
   while ((s0 += 16) < ns);
   if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel
   const int hh = row / a.bs, j = row % a.bs;
-  store_out(a, ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d, o / l);
+  const size_t e = ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d;
+  const f32x4_t v = o / l;
+  if (a.o_planes) {
+    uint16_t h[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = f32_to_bf16(v[i]);
+      lo[i] = f32_to_bf16(v[i] - bf16_to_f32(h[i]));
+    }
+    uint2 hw, lw;
+    hw.x = h[0] | (uint32_t(h[1]) << 16), hw.y = h[2] | (uint32_t(h[3]) << 16);
+    lw.x = lo[0] | (uint32_t(lo[1]) << 16), lw.y = lo[2] | (uint32_t(lo[3]) << 16);
+    *reinterpret_cast<uint2 *>(a.o_planes + e) = hw;
+    *reinterpret_cast<uint2 *>(a.o_planes + (size_t)a.B * a.bs * a.QH * D + e) = lw;
+  } else {
+    *reinterpret_cast<f32x4_t *>(a.o + e) = v;
+  }
 }
 
 // Merge of many splits (more than 16 per sequence: one long context): work-group = one
@@ -465,7 +514,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  const int R = a.bs * (a.QH / a.KVH), rpw = 256 / a.D;
+  const int R = a.bs * (a.QH / a.KVH), rpw = 1024 / a.D;  // (attn_merge_kernel's rows per work-group)
   {
     ProfScope prof("attn_merge", s);
     if (a.nsplit > 16)
