@@ -29,16 +29,6 @@ constexpr int kTileKeys = 64;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// element e of the merged output: fp32, or its (hi, lo) bf16 planes
-__device__ __forceinline__ void store_out(const AttnArgs &a, size_t e, float v) {
-  if (a.o_planes) {
-    const uint16_t h = f32_to_bf16(v);
-    a.o_planes[e] = h;
-    a.o_planes[(size_t)a.B * a.bs * a.QH * a.D + e] = f32_to_bf16(v - bf16_to_f32(h));
-  } else {
-    a.o[e] = v;
-  }
-}
 constexpr int kMaxChunk = 16 * kTileKeys;  // keys per split at most (attn_plan)
 
 template <typename T, int D>
@@ -320,30 +310,33 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnArgs a) {
   }
 }
 
-// Online log-sum-exp accumulation of up to 16 split partials (m, l, o) into a running
-// (m_acc, l_acc, o_acc) of one output element, in split order: the loads of all 16 are issued
-// before any is used, so one round trip covers 16 splits. The load addresses are clamped to
-// nmax (>= ns) splits; splits at or past ns are loaded but never used.
-__device__ __forceinline__ void merge16(const float *pm, const float *pl, const float *po, size_t stride_ml,
-                                        size_t stride_o, int s0, int step, int ns, int nmax, float &m_acc,
-                                        float &l_acc, float &o_acc) {
-  float mv[16], lv[16], pv[16];
+// Online log-sum-exp accumulation of NU split partials (m, l, o) into a running (m_acc, l_acc,
+// o_acc) of four consecutive output elements of one row, in split order: the splits s0, s0 +
+// step, ... whose loads (one 16-byte load of o per split) are all issued before any is used, so
+// one round trip covers NU splits. The load addresses are clamped to nmax (>= ns) splits; splits
+// at or past ns are loaded but never used.
+template <int NU>
+__device__ __forceinline__ void merge_x4(const float *pm, const float *pl, const float *po, size_t stride_ml,
+                                         size_t stride_o, int s0, int step, int ns, int nmax, float &m_acc,
+                                         float &l_acc, f32x4_t &o_acc) {
+  float mv[NU], lv[NU];
+  f32x4_t pv[NU];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
+  for (int u = 0; u < NU; ++u) {
     const int q = min(s0 + u * step, nmax - 1);
     mv[u] = pm[(size_t)q * stride_ml];
     lv[u] = pl[(size_t)q * stride_ml];
-    pv[u] = po[(size_t)q * stride_o];
+    pv[u] = *reinterpret_cast<const f32x4_t *>(po + (size_t)q * stride_o);
   }
   float m_new = m_acc;
 #pragma unroll
-  for (int u = 0; u < 16; ++u)
+  for (int u = 0; u < NU; ++u)
     if (s0 + u * step < ns) m_new = fmaxf(m_new, mv[u]);
   const float r = exp2f(m_acc - m_new);  // m_acc = -inf at first: r = 0 on empty sums
   l_acc *= r;
   o_acc *= r;
 #pragma unroll
-  for (int u = 0; u < 16; ++u)
+  for (int u = 0; u < NU; ++u)
     if (s0 + u * step < ns) {
       const float w = exp2f(mv[u] - m_new);
       l_acc += w * lv[u];
@@ -352,35 +345,24 @@ __device__ __forceinline__ void merge16(const float *pm, const float *pl, const 
   m_acc = m_new;
 }
 
-// merge16 for four consecutive output elements of one row (one 16-byte load per split): the
-// same operations, in the same order, for each of the four
-__device__ __forceinline__ void merge16x4(const float *pm, const float *pl, const float *po, size_t stride_ml,
-                                          size_t stride_o, int s0, int ns, int nmax, float &m_acc, float &l_acc,
-                                          f32x4_t &o_acc) {
-  float mv[16], lv[16];
-  f32x4_t pv[16];
+// element e.. e + 3 of the merged output: fp32 (one 16-byte store), or its (hi, lo) bf16 planes
+// (one 8-byte store each)
+__device__ __forceinline__ void store_out4(const AttnArgs &a, size_t e, f32x4_t v) {
+  if (a.o_planes) {
+    uint16_t h[4], lo[4];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int q = min(s0 + u, nmax - 1);
-    mv[u] = pm[(size_t)q * stride_ml];
-    lv[u] = pl[(size_t)q * stride_ml];
-    pv[u] = *reinterpret_cast<const f32x4_t *>(po + (size_t)q * stride_o);
-  }
-  float m_new = m_acc;
-#pragma unroll
-  for (int u = 0; u < 16; ++u)
-    if (s0 + u < ns) m_new = fmaxf(m_new, mv[u]);
-  const float r = exp2f(m_acc - m_new);
-  l_acc *= r;
-  o_acc *= r;
-#pragma unroll
-  for (int u = 0; u < 16; ++u)
-    if (s0 + u < ns) {
-      const float w = exp2f(mv[u] - m_new);
-      l_acc += w * lv[u];
-      o_acc += w * pv[u];
+    for (int i = 0; i < 4; ++i) {
+      h[i] = f32_to_bf16(v[i]);
+      lo[i] = f32_to_bf16(v[i] - bf16_to_f32(h[i]));
     }
-  m_acc = m_new;
+    uint2 hw, lw;
+    hw.x = h[0] | (uint32_t(h[1]) << 16), hw.y = h[2] | (uint32_t(h[3]) << 16);
+    lw.x = lo[0] | (uint32_t(lo[1]) << 16), lw.y = lo[2] | (uint32_t(lo[3]) << 16);
+    *reinterpret_cast<uint2 *>(a.o_planes + e) = hw;
+    *reinterpret_cast<uint2 *>(a.o_planes + (size_t)a.B * a.bs * a.QH * a.D + e) = lw;
+  } else {
+    *reinterpret_cast<f32x4_t *>(a.o + e) = v;
+  }
 }
 
 // Merge of up to 16 splits per sequence: thread (query row, 4 consecutive d) of a (sequence,
@@ -402,52 +384,38 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   // workspace's splits). Several: only the sequence's own splits are read.
   const int nmax = a.B == 1 ? a.nsplit : ns;
   int s0 = 0;
-  do merge16x4(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, ns, nmax, m, l, o);
+  do merge_x4<16>(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, 1, ns, nmax, m, l, o);
   while ((s0 += 16) < ns);
   if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel
   const int hh = row / a.bs, j = row % a.bs;
-  const size_t e = ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d;
-  const f32x4_t v = o / l;
-  if (a.o_planes) {
-    uint16_t h[4], lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = f32_to_bf16(v[i]);
-      lo[i] = f32_to_bf16(v[i] - bf16_to_f32(h[i]));
-    }
-    uint2 hw, lw;
-    hw.x = h[0] | (uint32_t(h[1]) << 16), hw.y = h[2] | (uint32_t(h[3]) << 16);
-    lw.x = lo[0] | (uint32_t(lo[1]) << 16), lw.y = lo[2] | (uint32_t(lo[3]) << 16);
-    *reinterpret_cast<uint2 *>(a.o_planes + e) = hw;
-    *reinterpret_cast<uint2 *>(a.o_planes + (size_t)a.B * a.bs * a.QH * D + e) = lw;
-  } else {
-    *reinterpret_cast<f32x4_t *>(a.o + e) = v;
-  }
+  store_out4(a, ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d, o / l);
 }
 
 // Merge of many splits (more than 16 per sequence: one long context): work-group = one
-// (sequence, kv head, query row). Thread (d, sub) accumulates the splits s = sub (mod 256 / D)
-// for element d, 16 loads in flight at a time; the sub-accumulators are then combined through
-// LDS in a fixed order.
+// (sequence, kv head, query row). Thread (d4, sub) accumulates four consecutive elements over
+// the splits s = sub (mod 1024 / D), 8 loads in flight at a time (one round trip up to 64
+// splits at D = 128); the sub-accumulators are then combined through LDS in a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge_rows_kernel(AttnArgs a) {
-  __shared__ float sm[4], sl[4], so[256];
+  __shared__ float sm[16], sl[16];
+  __shared__ f32x4_t so[256];
   const int row = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.QH / a.KVH;
-  const int D = a.D, nsub = 256 / D;
-  const int d = threadIdx.x % D, sub = threadIdx.x / D;
+  const int D = a.D, tpr = D / 4, nsub = 256 / tpr;  // D = 128: 32 threads a row, 8 subs; 64: 16, 16
+  const int t = (int)threadIdx.x % tpr, d = t * 4, sub = (int)threadIdx.x / tpr;
   const int c = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int ns = (c + a.bs + a.chunk - 1) / a.chunk;
   const size_t base = (size_t)(b * a.KVH + g) * a.nsplit * 64 + row;
-  float m = -INFINITY, l = 0.f, o = 0.f;
+  float m = -INFINITY, l = 0.f;
+  f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // as in attn_merge_kernel (a sub with no split adds nothing)
   const int nmax = a.B == 1 ? a.nsplit : ns;
   int s0 = sub;
-  do merge16(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, nsub, ns, nmax, m, l, o);
-  while ((s0 += 16 * nsub) < ns);
+  do merge_x4<8>(a.pm + base, a.pl + base, a.po + base * D + d, 64, 64 * (size_t)D, s0, nsub, ns, nmax, m, l, o);
+  while ((s0 += 8 * nsub) < ns);
   if (ns == 1) return;  // one split: normalised in place by attn_partial_kernel (uniform)
   so[threadIdx.x] = o;
-  if (d == 0) {
+  if (t == 0) {
     sm[sub] = m;
     sl[sub] = l;
   }
@@ -455,14 +423,15 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(AttnArgs a) {
   if (sub == 0) {
     float mm = -INFINITY;
     for (int q = 0; q < nsub; ++q) mm = fmaxf(mm, sm[q]);
-    float n = 0.f, dn = 0.f;
+    f32x4_t n = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float dn = 0.f;
     for (int q = 0; q < nsub; ++q) {
       const float w = exp2f(sm[q] - mm);  // a sub with no split: m = -inf, weight 0
-      n += w * so[q * D + d];
+      n += w * so[q * tpr + t];
       dn += w * sl[q];
     }
     const int hh = row / a.bs, j = row % a.bs;
-    store_out(a, ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d, n / dn);
+    store_out4(a, ((size_t)(b * a.bs + j) * a.QH + g * G + hh) * D + d, n / dn);
   }
 }
 
