@@ -74,6 +74,8 @@ def _compare_cache(spec, st, kc, vc, seqs):
     (SMALL_BF16, [1000], 48, True),
     (SMALL_BF16, [700, 33], 128, True),
     (SMALL_BF16, [4000], 16, True),
+    # head_dim 64, one sequence in 24 splits: the row-parallel merge with 16 split groups
+    (SMALL_BF16_D64, [3000], 16, True),
     (WIDE_TILE_BF16, WIDE_TILE_CTX, 16, True),
 ])
 def test_inject_and_propose_match_oracle(spec, ctx, P, shuffle):
