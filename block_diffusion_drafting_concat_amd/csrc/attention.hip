@@ -332,7 +332,10 @@ __device__ __forceinline__ void merge_x4(const float *pm, const float *pl, const
 #pragma unroll
   for (int u = 0; u < NU; ++u)
     if (s0 + u * step < ns) m_new = fmaxf(m_new, mv[u]);
-  const float r = exp2f(m_acc - m_new);  // m_acc = -inf at first: r = 0 on empty sums
+  // m_acc = -inf at first: r = 0 on empty sums; no split at all so far (a split group of the
+  // many-split merge with fewer splits than groups): m_acc = m_new = -inf, and r = 1 keeps the
+  // empty sums 0 (exp2f(-inf - -inf) would be NaN and poison the combination)
+  const float r = m_acc == m_new ? 1.f : exp2f(m_acc - m_new);
   l_acc *= r;
   o_acc *= r;
 #pragma unroll

@@ -76,6 +76,10 @@ def _compare_cache(spec, st, kc, vc, seqs):
     (SMALL_BF16, [4000], 16, True),
     # head_dim 64, one sequence in 24 splits: the row-parallel merge with 16 split groups
     (SMALL_BF16_D64, [3000], 16, True),
+    # a long and a short sequence: the many-split merge runs for both, and the short one's two
+    # splits leave most split groups empty (their sums must stay zero)
+    (SMALL_BF16, [4000, 100], 16, True),
+    (SMALL_BF16_D64, [3000, 100], 16, True),
     (WIDE_TILE_BF16, WIDE_TILE_CTX, 16, True),
 ])
 def test_inject_and_propose_match_oracle(spec, ctx, P, shuffle):
